@@ -1,0 +1,7 @@
+"""fp64 CPU oracle for the attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the product path.
+"""
+
+from .attention import decode, decode_split, prefill, prefill_rows  # noqa: F401

@@ -1,0 +1,143 @@
+"""Plain fp64 CPU oracle for exact attention (prefill and decode).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the HIP
+library and its Python binding) never calls it and has no CPU fallback.
+
+What it computes is the plain definition on page 3 of the pages ("What is
+Attention?", "The Problem", and the usage block under "Installation"): every
+query scores each visible key with a scaled dot product, the scores are turned
+into weights that are positive and sum to one, and the output row is the
+weight-averaged value rows.  There is no tiling and no online recurrence here:
+the method on the pages (page 3 "Kernel design"; page 2 "Technical details")
+reaches the same numbers by streaming tiles, which is exactly what this file is
+used to check.
+
+Conventions (readings of the pages, all explicit):
+  * inputs are the stored fp16/bf16 values converted exactly to float64;
+    ``scale`` is the float32 value that crosses the C interface, widened to
+    float64;
+  * causal: key j is visible to query row i iff j <= i (one sequence length for
+    queries and keys);
+  * decode over a cache of length L attends to rows 0..L-1, the current token's
+    own row included, so decode with L = t + 1 equals causal prefill row t
+    (page 3, "What can it do": decoding token t equals prefill row t);
+  * masked scores are -inf, i.e. exactly zero weight.
+
+Every function follows the definition above; ``decode_split`` additionally
+follows the split-and-merge description on page 3 ("Kernel design": split-K
+decode with partial (m, l, acc) merged exactly by a second pass) and is used only
+to pin split-size invariance.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 1024  # rows per matrix product; row blocking does not change any row's value
+
+
+def _softmax_average(s: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Rows of weights exp(s - max) / sum, applied to v.  s: (R, K) with -inf allowed."""
+    m = np.max(s, axis=1, keepdims=True)
+    w = np.exp(s - m)
+    l = np.sum(w, axis=1, keepdims=True)
+    return (w @ v) / l
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float) -> np.ndarray:
+    """Exact attention for (B, H, N, d) float64 arrays; returns (B, H, N, d) float64.
+
+    Page 3, "What is Attention?" / "The Problem": each row scores every
+    (previous, if causal) key; the weights sum to one and combine the values.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    assert k.shape == (B, H, N, d) and v.shape == (B, H, N, d)
+    out = np.empty((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, ROW_BLOCK):
+                rows = np.arange(r0, min(N, r0 + ROW_BLOCK))
+                out[b, h, rows] = _rows(q[b, h], k[b, h], v[b, h], rows, causal, scale)
+    return out
+
+
+def _rows(qh, kh, vh, rows, causal, scale):
+    s = float(scale) * (qh[rows] @ kh.T)  # (R, N)
+    if causal:
+        keys = np.arange(kh.shape[0])
+        s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+    return _softmax_average(s, vh)
+
+
+def prefill_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:
+    """The same definition for selected rows of one (b, h) only; returns (len(rows), d).
+
+    Used to check outputs at sizes where the full oracle would take minutes.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    qh = np.asarray(q[b, h], dtype=np.float64)
+    kh = np.asarray(k[b, h], dtype=np.float64)
+    vh = np.asarray(v[b, h], dtype=np.float64)
+    return _rows(qh, kh, vh, rows, causal, scale)
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float) -> np.ndarray:
+    """One query row per (b, h) over the first L_b cache rows; returns (B, H, 1, d).
+
+    Page 3, "What can it do": one new token attends over a KV cache, with a
+    different current length per sequence in the batch.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, H, one, d = q.shape
+    assert one == 1
+    out = np.empty((B, H, 1, d), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        assert 1 <= L <= kc.shape[2], "cache length must lie in [1, max_len]"
+        for h in range(H):
+            s = float(scale) * (q[b, h] @ kc[b, h, :L].T)  # (1, L)
+            out[b, h] = _softmax_average(s, vc[b, h, :L])
+    return out
+
+
+def decode_split(q, k_cache, v_cache, seq_lens, scale: float, chunk: int) -> np.ndarray:
+    """Decode computed as chunks of ``chunk`` cache rows, then merged exactly.
+
+    Page 3, "Kernel design": the cache is split into chunks, each chunk yields a
+    partial (m, l, acc), and a second pass merges the partials with the (m, l)
+    rescale.  For chunk c over rows J_c: m_c = max s, l_c = sum exp(s - m_c),
+    a_c = sum exp(s - m_c) v.  With M = max_c m_c the result is
+    sum_c exp(m_c - M) a_c / sum_c exp(m_c - M) l_c.  Empty chunks do not exist
+    here because chunks only cover [0, L).
+    """
+    assert chunk >= 1
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, H, _, d = q.shape
+    out = np.empty((B, H, 1, d), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        assert 1 <= L <= kc.shape[2]
+        for h in range(H):
+            ms, ls, accs = [], [], []
+            for c0 in range(0, L, chunk):
+                c1 = min(L, c0 + chunk)
+                s = float(scale) * (kc[b, h, c0:c1] @ q[b, h, 0])  # (C,)
+                m = np.max(s)
+                p = np.exp(s - m)
+                ms.append(m)
+                ls.append(np.sum(p))
+                accs.append(p @ vc[b, h, c0:c1])
+            M = max(ms)
+            wts = [np.exp(m - M) for m in ms]
+            num = sum(w * a for w, a in zip(wts, accs))
+            den = sum(w * l for w, l in zip(wts, ls))
+            out[b, h, 0] = num / den
+    return out

@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in copies of the oracle and check a pin catches each.
+
+The mutants are built on the CPU from the oracle's own source text with one
+substitution each; the real oracle is never modified.
+"""
+
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTATIONS = {
+    "mask_strict": ("keys[None, :] <= rows[:, None]", "keys[None, :] < rows[:, None]"),
+    "mask_reversed": ("keys[None, :] <= rows[:, None]", "keys[None, :] >= rows[:, None]"),
+    "dropped_scale": ("s = float(scale) * (qh[rows] @ kh.T)", "s = (qh[rows] @ kh.T)"),
+    "swapped_qk": ("s = float(scale) * (qh[rows] @ kh.T)", "s = float(scale) * (kh[rows] @ qh.T)"),
+    "no_max_subtraction": ("w = np.exp(s - m)", "w = np.exp(s)"),
+    "no_normalisation": ("return (w @ v) / l", "return (w @ v)"),
+    "wrong_sum_axis": ("l = np.sum(w, axis=1, keepdims=True)", "l = np.sum(w, axis=0, keepdims=True)"),
+    "reversed_values": ("return (w @ v) / l", "return (w @ v[::-1]) / l"),
+    "decode_excludes_current": ("(q[b, h] @ kc[b, h, :L].T)", "(q[b, h] @ kc[b, h, :L - 1].T)"),
+    "decode_values_offset": ("out[b, h] = _softmax_average(s, vc[b, h, :L])", "out[b, h] = _softmax_average(s, vc[b, h, 1:L + 1])"),
+    "split_no_rescale": ("wts = [np.exp(m - M) for m in ms]", "wts = [1.0 for m in ms]"),
+    "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
+    "split_sign": ("wts = [np.exp(m - M) for m in ms]", "wts = [np.exp(M - m) for m in ms]"),
+    "split_drops_last_row": ("c1 = min(L, c0 + chunk)", "c1 = min(L - 1, c0 + chunk)"),
+}
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(text.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutant(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for pin in oracle_pins.PINS:
+        try:
+            with __import__("numpy").errstate(all="ignore"):
+                pin(mod)
+        except Exception:  # an AssertionError, or the broken code raising on its own
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
