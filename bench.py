@@ -1,0 +1,264 @@
+"""Benchmark of the attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  * prefill at the headline shape: B=1, H=16, N=16384, d=128, bf16, non-causal,
+    scale 1/sqrt(128) (the dense d=128 comparison on page 1 at 16K tokens);
+  * decode over the ragged batch: B=8, H=12, d=64, fp16, cache 4096 rows, lengths
+    uniform in [1, 4096] from seed 0 (page 3, "What can it do": a different current
+    length per sequence), split-K with the automatic chunk, then the merge.
+Inputs are made once from seed 0 and are resident in HBM before timing starts.
+W untimed steps, then K timed steps between two device synchronisations.
+
+Prints ONE JSON line.  `value` is prefill TFLOP/s over the whole timed region
+(algorithmic flop 4*B*H*N*N*d per step / wall time per step, decode included in the
+time).  `roofline` covers the prefill kernel, timed with HIP events on the stream it
+runs on.  `decode` reports the decode path's HBM rate, timed with events after a
+512 MiB write that evicts the L2 and the Infinity Cache before every call.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+COUNTERS = os.path.join(ROOT, "profiles", "prefill_headline_counters.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "exact_attention_prefill_amd", "csrc", f)
+    for f in ("prefill.hip", "attn_device.h")
+]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter runs, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_sha") != kernel_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, scale, budget_s):
+    """Time the fp64 oracle on whole heads of the headline prefill until budget_s passes."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # threadpoolctl missing: report the host count
+        cores = os.cpu_count()
+    N, d = q.shape[2], q.shape[3]
+    rows_per_block = 2048
+    done_rows, t_total = 0, 0.0
+    h = 0
+    while t_total < budget_s and h < q.shape[1]:
+        qh, kh, vh = (t[0, h].to(torch.float64).numpy()[None, None] for t in (q, k, v))
+        for r0 in range(0, N, rows_per_block):
+            rows = np.arange(r0, min(N, r0 + rows_per_block))
+            t0 = time.perf_counter()
+            oracle.prefill_rows(qh, kh, vh, False, scale, 0, 0, rows)
+            t_total += time.perf_counter() - t0
+            done_rows += len(rows)
+            if t_total >= budget_s:
+                break
+        h += 1
+    flop = 4.0 * done_rows * N * d
+    return {
+        "value": flop / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done_rows} query rows (of head 0 onward) of the B=1 H=16 N=16384 d=128 bf16 non-causal "
+        f"prefill, fp64 NumPy, {t_total:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU only: the attention forward here is a single-GPU kernel library "
+            f"(--gpus {args.gpus} is not supported; run with --gpus 1)",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_prefill_amd as ea
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+
+    P = W.HEADLINE
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {cus} CUs; making inputs")
+    qc, kc, vc = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=0)
+    q, k, v = (t.to(dev) for t in (qc, kc, vc))
+    out = torch.empty_like(q)
+
+    D = W.DECODE[1]
+    dq, dk, dv, dl = W.decode_inputs(D.B, D.H, D.max_len, D.d, D.dtype, seed=0)
+    dq_, dk_, dv_, dl_ = (t.to(dev) for t in (dq, dk, dv, dl))
+    dout = torch.empty_like(dq_)
+    chunk, n_split = ea.decode_choose_split(D.B, D.H, D.max_len, D.d, cus)
+    ws = torch.empty(ea.decode_workspace_bytes(D.B, D.H, n_split, D.d), dtype=torch.uint8, device=dev)
+    dec_bytes = W.decode_bytes(D.H, D.d, dl.tolist())
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out)
+        if ev:
+            ev[1].record()
+        ea.decode(dq_, dk_, dv_, dl_, scale=D.scale, out=dout, chunk=chunk, workspace=ws)
+        if ev:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms_warm = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    pre_mean = float(np.mean(pre_ms))
+    pre_tflops = P.flop / (pre_mean * 1e-3) / 1e12
+    value = P.flop / (ms_per_step * 1e-3) / 1e12
+    log(f"prefill {pre_mean:.3f} ms/launch = {pre_tflops:.1f} TFLOP/s; step {ms_per_step:.3f} ms")
+
+    # Decode, cold: evict L2 and the 256 MB Infinity Cache with a 512 MiB write first.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.decode_iters):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ea.decode(dq_, dk_, dv_, dl_, scale=D.scale, out=dout, chunk=chunk, workspace=ws)
+        b.record()
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold_us = float(np.mean([a.elapsed_time(b) for a, b in cold])) * 1e3
+    warm_us = float(np.mean(dec_ms_warm)) * 1e3
+    dec_gbs = dec_bytes / (cold_us * 1e-6) / 1e9
+    log(f"decode cold {cold_us:.2f} us = {dec_gbs:.0f} GB/s; warm {warm_us:.2f} us")
+
+    # Parity spot check of this run's outputs against the oracle (sampled rows).
+    import oracle
+
+    rows = W.prefill_rows_sample(P.N, 16, 0)
+    perr = 0.0
+    for h in (0, P.H - 1):
+        f = lambda t: t[0, h].to(torch.float64).numpy()[None, None]  # noqa: E731
+        ref = oracle.prefill_rows(f(qc), f(kc), f(vc), P.causal, P.scale, 0, 0, rows)
+        got = out[0, h, rows].to(torch.float64).cpu().numpy()
+        perr = max(perr, float(np.max(np.abs(got - ref))))
+    dref = oracle.decode(dq.double().numpy(), dk.double().numpy(), dv.double().numpy(), dl.numpy(), D.scale)
+    derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
+    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(qc, kc, vc, P.scale, args.cpu_seconds)
+
+    traffic = measured_traffic()
+    rec = {
+        "metric": "prefill TFLOP/s & % MFMA peak (d=128, N=16K); decode HBM GB/s & % peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill B=1 H=16 N=16384 d=128 bf16 non-causal + decode B=8 H=12 d=64 fp16 ragged cache 4096",
+            "prefill": {"B": P.B, "H": P.H, "N": P.N, "d": P.d, "dtype": P.dtype, "causal": P.causal},
+            "decode": {"B": D.B, "H": D.H, "max_len": D.max_len, "d": D.d, "dtype": D.dtype,
+                       "seq_lens": dl.tolist(), "chunk": chunk, "n_split": n_split},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "decode": {
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "us_cold": round(cold_us, 3),
+            "us_warm": round(warm_us, 3),
+            "bytes": dec_bytes,
+        },
+        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Python binding of the gfx950 attention library (libattn.so).
+
+Same names and argument order as the two calls on page 3 of the pages
+("Installation": ``prefill(q, k, v, causal, scale)`` and
+``decode(q, k_cache, v_cache, seq_lens, scale)``).  This layer only marshals
+arguments: it checks tensor metadata, passes device pointers and the current
+HIP stream through ctypes, and turns a negative status into an exception.  Every
+step of the computation runs in the library's HIP kernels; there is no fallback.
+PyTorch supplies device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F16, ATTN_BF16 = 0, 1
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGNMENT, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = -1, -2, -3, -4, -5
+DECODE_ROW_GRANULE = 32
+
+# Every symbol include/attn.h declares.
+EXPORTS = (
+    "attn_prefill",
+    "attn_decode",
+    "attn_decode_ex",
+    "attn_decode_choose_split",
+    "attn_decode_workspace_bytes",
+    "attn_status_string",
+    "attn_last_error",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+class AttnValueError(AttnError, ValueError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m exact_attention_prefill_amd.build` "
+                "(the HIP library is the only implementation)"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        L.attn_prefill.restype = i
+        L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        L.attn_decode.restype = i
+        L.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_decode_ex.restype = i
+        L.attn_decode_choose_split.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.attn_decode_choose_split.restype = i
+        L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+        L.attn_decode_workspace_bytes.restype = sz
+        L.attn_status_string.argtypes = [i]
+        L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        L = lib()
+        detail = L.attn_last_error().decode() or L.attn_status_string(status).decode()
+        cls = AttnValueError if status in (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGNMENT) else AttnError
+        raise cls(status, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise AttnValueError(ATTN_ERR_INVALID_ARG, f"dtype {t.dtype} is not float16/bfloat16")
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype, shape) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, f"{name} must be a GPU tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """Exact attention for (B, H, N, d) fp16/bf16 GPU tensors; returns out (same shape/dtype)."""
+    if q.dim() != 4:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q must be (batch, heads, seq_len, d)")
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    ptrs = [_dev_tensor(t, n, q.dtype, (B, H, N, d)) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    with torch.cuda.device(q.device):
+        _check(lib().attn_prefill(*ptrs, B, H, N, d, dt, int(bool(causal)), float(scale), _stream(q.device)))
+    return out
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, chunk: int = 0, workspace=None,
+           validate: bool = False):
+    """One query row per (b, h) over the first seq_lens[b] cache rows.
+
+    q (B, H, 1, d); caches (B, H, max_len, d); seq_lens int32 GPU tensor (B,).
+    ``chunk``/``workspace`` select attn_decode_ex (0 = automatic chunk; workspace a
+    GPU tensor of at least decode_workspace_bytes bytes).  ``validate`` checks on the
+    host that every length lies in [1, max_len] (a device-to-host copy).
+    """
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q must be (batch, heads, 1, d)")
+    B, H, _, d = q.shape
+    if k_cache.dim() != 4:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "k_cache must be (batch, heads, max_len, d)")
+    max_len = k_cache.shape[2]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    pq = _dev_tensor(q, "q", q.dtype, (B, H, 1, d))
+    pk = _dev_tensor(k_cache, "k_cache", q.dtype, (B, H, max_len, d))
+    pv = _dev_tensor(v_cache, "v_cache", q.dtype, (B, H, max_len, d))
+    pl = _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    po = _dev_tensor(out, "out", q.dtype, (B, H, 1, d))
+    if validate:
+        lens = seq_lens.cpu()
+        if int(lens.min()) < 1 or int(lens.max()) > max_len:
+            raise AttnValueError(ATTN_ERR_INVALID_ARG, f"seq_lens must lie in [1, {max_len}]")
+    with torch.cuda.device(q.device):
+        st = _stream(q.device)
+        if chunk == 0 and workspace is None:
+            _check(lib().attn_decode(pq, pk, pv, pl, po, B, H, max_len, d, dt, float(scale), st))
+        else:
+            wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+            if workspace is not None and workspace.device.type != "cuda":
+                raise AttnValueError(ATTN_ERR_INVALID_ARG, "workspace must be a GPU tensor")
+            _check(lib().attn_decode_ex(pq, pk, pv, pl, po, B, H, max_len, d, dt, float(scale), int(chunk),
+                                        wp or None, wb, st))
+    return out
+
+
+def decode_choose_split(B: int, H: int, max_len: int, d: int, num_cus: int):
+    """(chunk, n_split) the automatic decode split picks for a device with num_cus CUs."""
+    c, n = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().attn_decode_choose_split(B, H, max_len, d, num_cus, ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value
+
+
+def decode_workspace_bytes(B: int, H: int, n_split: int, d: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H, n_split, d))
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().attn_last_error().decode()

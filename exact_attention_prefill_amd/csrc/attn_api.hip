@@ -1,0 +1,193 @@
+// C-ABI of the attention library: argument validation, status codes, the decode
+// split chooser, workspace handling and dispatch to the gfx950 kernels.  Every
+// argument is checked before any HIP call; nothing throws across the interface.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "attn.h"
+
+namespace attn {
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int dt,
+                          int causal, float scale, hipStream_t s);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
+                         int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws, hipStream_t st);
+}  // namespace attn
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int B, int H, int rows, int d, int dtype, float scale, const char* rows_name) {
+  if (B < 1 || H < 1 || rows < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "B=%d, H=%d and %s=%d must all be >= 1", B, H, rows_name, rows);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "dtype %d is not ATTN_F16/ATTN_BF16", dtype);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (64 or 128)", d);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  // Element offsets are formed in 64 bits, but per-head row counts and grid sizes stay in int.
+  const long long elems = (long long)B * H * rows;
+  if (elems > (1LL << 40) / d) return fail(ATTN_ERR_INVALID_ARG, "tensor too large");
+  return ATTN_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(ATTN_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(ATTN_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0) return fail(ATTN_ERR_HIP, "compute-unit count query failed: %s", hipGetErrorString(e));
+    cached[dev] = n;
+  }
+  *cus = cached[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int dtype,
+                 int causal, float scale, void* stream) {
+  int st;
+  if ((st = check_common(B, H, N, d, dtype, scale, "N")) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
+    return st;
+  if (out == q || out == k || out == v) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
+  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, N, d, dtype, causal, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {
+  if (B < 1 || H < 1 || max_len < 1 || num_cus < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "B, H, max_len and num_cus must be >= 1");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (64 or 128)", d);
+  if (!chunk || !n_split) return fail(ATTN_ERR_INVALID_ARG, "chunk and n_split must be non-NULL host pointers");
+  const long long T = ATTN_DECODE_ROW_GRANULE;
+  const long long pairs = (long long)B * H;
+  const long long target = (long long)ATTN_DECODE_WGS_PER_CU * num_cus;
+  const long long max_splits = (max_len + T - 1) / T;
+  long long ns = (target + pairs - 1) / pairs;
+  if (ns < 1) ns = 1;
+  if (ns > max_splits) ns = max_splits;
+  long long c = (max_len + ns - 1) / ns;
+  c = (c + T - 1) / T * T;
+  // Rounding the chunk up to the granule can drop the split count below the target;
+  // shrink it one granule at a time until the target is met again.
+  while (c > T && pairs * ((max_len + c - 1) / c) < target) c -= T;
+  *chunk = (int)c;
+  *n_split = (int)((max_len + c - 1) / c);
+  return ok();
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d) {
+  if (B < 1 || H < 1 || n_split < 1 || d < 1) return 0;
+  return (size_t)B * H * n_split * (size_t)(d + 2) * sizeof(float);
+}
+
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                       int B, int H, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
+                       size_t ws_bytes, void* stream, bool caller_ws) {
+  int st;
+  if ((st = check_common(B, H, max_len, d, dtype, scale, "max_len")) != ATTN_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
+      (st = check_ptr(out, "out")))
+    return st;
+  if (!seq_lens) return fail(ATTN_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (((uintptr_t)seq_lens & 3u) != 0) return fail(ATTN_ERR_ALIGNMENT, "seq_lens is not 4-byte aligned");
+  if (out == q || out == k_cache || out == v_cache) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
+  const int T = ATTN_DECODE_ROW_GRANULE;
+  const int cap = (max_len + T - 1) / T * T;
+  if (chunk != 0 && (chunk < T || chunk % T != 0 || chunk > cap))
+    return fail(ATTN_ERR_INVALID_ARG, "chunk=%d must be 0 or a multiple of %d in [%d, %d]", chunk, T, T, cap);
+  if (caller_ws && workspace && !aligned16(workspace)) return fail(ATTN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (caller_ws && !workspace && ws_bytes != 0) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but ws_bytes > 0");
+
+  int n_split = 0;
+  if (chunk == 0) {
+    int cus = 0;
+    if ((st = device_cus(&cus)) != ATTN_OK) return st;
+    if ((st = attn_decode_choose_split(B, H, max_len, d, cus, &chunk, &n_split)) != ATTN_OK) return st;
+  } else {
+    n_split = (max_len + chunk - 1) / chunk;
+  }
+  const size_t need = attn_decode_workspace_bytes(B, H, n_split, d);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  bool own = false;
+  if (!caller_ws || (workspace == nullptr && ws_bytes == 0)) {
+    hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", need, hipGetErrorString(e));
+    own = true;
+  } else if (ws_bytes < need) {
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  }
+  hipError_t e = attn::launch_decode(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, chunk,
+                                     n_split, (float*)ws, s);
+  if (own) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, int B,
+                int H, int max_len, int d, int dtype, float scale, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, 0, nullptr, 0, stream, false);
+}
+
+int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, int B,
+                   int H, int max_len, int d, int dtype, float scale, int chunk, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, chunk, workspace, ws_bytes,
+                     stream, true);
+}
+
+}  // extern "C"

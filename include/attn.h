@@ -1,0 +1,117 @@
+/*
+ * attn.h - C interface of the MI355X (gfx950) exact attention forward library.
+ *
+ * The operation is exact softmax attention, O = softmax(scale * Q K^T [causal mask]) V,
+ * as defined on the flash-attention-cuda README (page 3, "What is Attention?" and
+ * "The Problem"), computed tile by tile with an online softmax so that the N x N
+ * score table never reaches device memory (page 3, "What is Flash Attention?" and
+ * "Kernel design"; page 2, "Technical details").
+ *
+ * Two paths, matching the two calls of page 3's "Installation" usage block:
+ *   attn_prefill - the prompt phase: batched, multi-head, causal or full attention;
+ *   attn_decode  - the generation phase: one new query row per (batch, head) over a
+ *                  KV cache whose current length differs per sequence, computed as a
+ *                  split-K pass that writes partial (m, l, acc) per chunk, then an
+ *                  exact merge pass with no atomics (page 3, "Kernel design").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major (batch, heads, rows, d) with d fastest, no strides.
+ *     All tensors of one call share one element type (attn_dtype); the output has the
+ *     input's type, rounded from fp32 to nearest-even.
+ *   - Pointers are DEVICE pointers (except where a parameter says host) owned by the
+ *     caller; they must be non-null and 16-byte aligned.  The library keeps no
+ *     allocation and no state between calls other than a thread-local error text and
+ *     a per-device compute-unit count.
+ *   - `stream` is a hipStream_t (NULL selects the default stream).  Calls enqueue
+ *     work on it and return without waiting; kernel faults surface on later
+ *     synchronisation, launch failures are reported as ATTN_ERR_HIP.
+ *   - Every argument is validated before any HIP call; an invalid call returns a
+ *     negative status, enqueues nothing and sets attn_last_error().
+ *   - scale may be any finite float (the pages pass 1/8 for d = 64).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* a size, flag, pointer or scale outside its domain   */
+  ATTN_ERR_UNSUPPORTED = -2, /* a head dimension or dtype this build has no kernel for */
+  ATTN_ERR_ALIGNMENT = -3,   /* a pointer not 16-byte aligned                          */
+  ATTN_ERR_WORKSPACE = -4,   /* caller workspace too small                             */
+  ATTN_ERR_HIP = -5          /* the HIP runtime refused a launch or an allocation      */
+} attn_status;
+
+/* Prefill (page 3, "What can it do": prompt phase; "Installation": prefill(q, k, v,
+ * causal, scale)).
+ *   q, k, v : [B][H][N][d] inputs;  out : [B][H][N][d] output, must not alias an input.
+ *   B, H, N >= 1;  d in {64, 128};  dtype ATTN_F16 or ATTN_BF16;  causal in {0, 1}
+ *   (1: key j is visible to query row i iff j <= i).
+ * Allocates nothing.  Returns ATTN_OK or a negative attn_status. */
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                 int dtype, int causal, float scale, void* stream);
+
+/* Decode (page 3, "What can it do": generation phase; "Installation": decode(q,
+ * k_cache, v_cache, seq_lens, scale)).
+ *   q        : [B][H][1][d] one query row per sequence and head;
+ *   k_cache, v_cache : [B][H][max_len][d];
+ *   seq_lens : DEVICE int32 [B]; sequence b attends to cache rows 0 .. seq_lens[b]-1
+ *              (the current token's own row included, so decoding token t with
+ *              seq_lens = t + 1 equals causal prefill row t).  Valid lengths are
+ *              1 .. max_len; the kernels clamp other values into [0, max_len] for
+ *              memory safety and write zeros for a length of 0.
+ *   out      : [B][H][1][d].
+ * The chunk size is chosen at launch (attn_decode_choose_split with this device's
+ * compute-unit count).  The partials live in a workspace taken with hipMallocAsync and
+ * released with hipFreeAsync on `stream` (stream ordered, no synchronisation). */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                void* out, int B, int H, int max_len, int d, int dtype, float scale, void* stream);
+
+/* Decode with a caller-chosen chunk and caller-owned workspace.
+ *   chunk     : cache rows per split; 0 selects the automatic choice, otherwise it must
+ *               be a multiple of ATTN_DECODE_ROW_GRANULE in [granule, roundup(max_len,
+ *               granule)] (every such chunk gives the same result up to fp32 rounding).
+ *   workspace : DEVICE buffer of at least attn_decode_workspace_bytes(B, H, n_split, d)
+ *               bytes (n_split = ceil(max_len / chunk)), 16-byte aligned; its contents on
+ *               entry do not matter.  May be NULL only when ws_bytes is 0, which asks the
+ *               call to behave like attn_decode (stream-ordered allocation).
+ * Returns ATTN_ERR_WORKSPACE if ws_bytes is too small. */
+int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                   void* out, int B, int H, int max_len, int d, int dtype, float scale, int chunk,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Rows of the decode split kernel's work granule: legal chunk sizes are multiples of it. */
+#define ATTN_DECODE_ROW_GRANULE 32
+
+/* Split workgroups per compute unit that the automatic decode split aims for. */
+#define ATTN_DECODE_WGS_PER_CU 2
+
+/* Host-only: the automatic decode split (page 3, "Kernel design": the chunk size is
+ * chosen at launch so that even batch size 1 fills the GPU).  Aims at
+ * ATTN_DECODE_WGS_PER_CU split workgroups per compute unit over the B*H (sequence,
+ * head) pairs.  Writes the chunk (rows, a multiple of the granule) and the number of
+ * splits to the HOST pointers chunk and n_split.  No HIP call. */
+int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split);
+
+/* Host-only: bytes of decode workspace for B*H*n_split partials of (m, l, acc[d]) fp32. */
+size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d);
+
+/* Host-only: a static description of a status code. */
+const char* attn_status_string(int status);
+
+/* Host-only: thread-local detail for the last non-OK return on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

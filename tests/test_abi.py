@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects
+invalid arguments before any HIP call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_prefill_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Fake, 16-byte aligned "device" addresses: validation must fail before they are used.
+P = [0x10000 + 0x100 * i for i in range(8)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(ea.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ea.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert getattr(L, name) is not None
+
+
+def _prefill(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, N=128, d=64, dt=0, causal=0, scale=0.125, s=None)
+    a.update(kw)
+    return ea.lib().attn_prefill(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["N"], a["d"], a["dt"],
+                                 a["causal"], a["scale"], a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(B=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(H=-1), ea.ATTN_ERR_INVALID_ARG),
+        (dict(N=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=32), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(dt=2), ea.ATTN_ERR_INVALID_ARG),
+        (dict(causal=2), ea.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), ea.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), ea.ATTN_ERR_INVALID_ARG),
+        (dict(q=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(out=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(k=P[1] + 8), ea.ATTN_ERR_ALIGNMENT),
+        (dict(out=P[0]), ea.ATTN_ERR_INVALID_ARG),
+        (dict(out=P[2]), ea.ATTN_ERR_INVALID_ARG),
+    ],
+)
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+    assert ea.last_error() != ""
+
+
+def _decode_ex(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], lens=P[4], out=P[3], B=2, H=3, max_len=100, d=64, dt=0, scale=0.125,
+             chunk=32, ws=P[5], ws_bytes=1 << 20, s=None)
+    a.update(kw)
+    return ea.lib().attn_decode_ex(a["q"], a["k"], a["v"], a["lens"], a["out"], a["B"], a["H"], a["max_len"],
+                                   a["d"], a["dt"], a["scale"], a["chunk"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(B=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(max_len=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(lens=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(lens=P[4] + 2), ea.ATTN_ERR_ALIGNMENT),
+        (dict(chunk=16), ea.ATTN_ERR_INVALID_ARG),
+        (dict(chunk=33), ea.ATTN_ERR_INVALID_ARG),
+        (dict(chunk=160), ea.ATTN_ERR_INVALID_ARG),  # above roundup(100, 32) = 128
+        (dict(chunk=-32), ea.ATTN_ERR_INVALID_ARG),
+        (dict(ws=P[5] + 4), ea.ATTN_ERR_ALIGNMENT),
+        (dict(ws=None, ws_bytes=64), ea.ATTN_ERR_INVALID_ARG),
+        (dict(ws_bytes=100), ea.ATTN_ERR_WORKSPACE),
+        (dict(scale=float("-inf")), ea.ATTN_ERR_INVALID_ARG),
+        (dict(out=P[1]), ea.ATTN_ERR_INVALID_ARG),
+    ],
+)
+def test_decode_validation(kw, status):
+    assert _decode_ex(**kw) == status
+    assert ea.last_error() != ""
+
+
+def test_decode_workspace_check_is_exact():
+    need = ea.decode_workspace_bytes(2, 3, 4, 64)  # max_len 100, chunk 32 -> 4 splits
+    assert need == 2 * 3 * 4 * 66 * 4
+    assert _decode_ex(ws_bytes=need - 1) == ea.ATTN_ERR_WORKSPACE
+
+
+def test_plain_decode_validation():
+    L = ea.lib()
+    assert L.attn_decode(P[0], P[1], P[2], P[4], P[3], 1, 1, 0, 64, 0, 0.125, None) == ea.ATTN_ERR_INVALID_ARG
+    assert L.attn_decode(P[0], P[1], P[2], P[4], P[3], 1, 1, 8, 80, 0, 0.125, None) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert ea.status_string(s) and ea.status_string(s) != "unknown status"
+    assert ea.status_string(7) == "unknown status"
+
+
+def test_last_error_is_thread_local():
+    import threading
+
+    assert _prefill(B=0) == ea.ATTN_ERR_INVALID_ARG
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(ea.last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert ea.last_error() != ""
+
+
+def test_workspace_bytes():
+    assert ea.decode_workspace_bytes(8, 12, 6, 64) == 8 * 12 * 6 * 66 * 4
+    assert ea.decode_workspace_bytes(0, 12, 6, 64) == 0

@@ -1,0 +1,51 @@
+"""Host logic of the automatic decode split (no GPU): page 3, "Kernel design" - the
+chunk is chosen at launch so that even batch size 1 fills every compute unit."""
+
+import itertools
+
+import pytest
+
+import exact_attention_prefill_amd as ea
+
+WGS_PER_CU = 2
+G = ea.DECODE_ROW_GRANULE
+
+
+@pytest.mark.parametrize(
+    "B,H,max_len,cus", list(itertools.product([1, 2, 8, 64], [1, 12, 32], [1, 31, 32, 33, 1000, 4096, 131072], [82, 256]))
+)
+def test_split_is_legal_and_covers(B, H, max_len, cus):
+    chunk, n = ea.decode_choose_split(B, H, max_len, 64, cus)
+    assert chunk % G == 0 and chunk >= G
+    assert chunk <= -(-max_len // G) * G
+    assert n == -(-max_len // chunk)
+    assert (n - 1) * chunk < max_len <= n * chunk
+    # Enough splits to give every CU its share, unless the cache is too short to split further.
+    if n * B * H < WGS_PER_CU * cus:
+        assert chunk == G
+
+
+def test_batch_one_fills_the_chip():
+    chunk, n = ea.decode_choose_split(1, 12, 4096, 64, 256)
+    assert (chunk, n) == (96, 43)
+    assert 12 * n >= 2 * 256
+
+
+def test_batch_eight():
+    assert ea.decode_choose_split(8, 12, 4096, 64, 256) == (704, 6)
+
+
+def test_more_cus_never_larger_chunks():
+    prev = None
+    for cus in (32, 64, 82, 128, 256, 304):
+        c, _ = ea.decode_choose_split(1, 12, 4096, 64, cus)
+        assert prev is None or c <= prev
+        prev = c
+
+
+@pytest.mark.parametrize("bad", [dict(B=0), dict(H=0), dict(max_len=0), dict(cus=0), dict(d=48)])
+def test_chooser_rejects(bad):
+    a = dict(B=1, H=1, max_len=10, d=64, cus=10)
+    a.update(bad)
+    with pytest.raises(ValueError):
+        ea.decode_choose_split(a["B"], a["H"], a["max_len"], a["d"], a["cus"])

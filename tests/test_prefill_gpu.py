@@ -1,0 +1,157 @@
+"""Prefill on the GPU against the fp64 oracle, through the C-ABI library."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_prefill_amd as ea
+import oracle
+import workloads as W
+from parity import check, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run(q, k, v, causal, scale):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def full_parity(B, H, N, d, dtype, causal, scale, seed):
+    q, k, v = W.prefill_inputs(B, H, N, d, dtype, seed)
+    out = run(q, k, v, causal, scale)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal, scale)
+    return check(f64(out), ref, dtype, f"B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("case", W.SMALL_F16, ids=lambda c: c.name)
+def test_small_config(case, seed):
+    full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 63, 64, 65, 127, 128, 129, 200, 333])
+def test_ragged_lengths(N, causal, d, dtype):
+    scale = 1.0 / np.sqrt(d)
+    full_parity(2, 3, N, d, dtype, causal, scale, seed=N)
+
+
+@pytest.mark.parametrize("case", W.GPT2_F16, ids=lambda c: c.name)
+def test_gpt2_config(case):
+    full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed=0)
+
+
+@pytest.mark.parametrize("case", [c for c in W.GPT2_SWEEP if c.N <= 1024], ids=lambda c: c.name)
+def test_gpt2_sweep(case):
+    full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed=1)
+
+
+def sampled_parity(case, seed, heads, nrows):
+    q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed)
+    out = run(q, k, v, case.causal, case.scale)
+    worst = 0.0
+    rows = W.prefill_rows_sample(case.N, nrows, seed)
+    for (b, h) in heads:
+        # widen only the sampled head to fp64; the oracle reads just these rows of q
+        ref = oracle.prefill_rows(f64(q[b, h])[None, None], f64(k[b, h])[None, None], f64(v[b, h])[None, None],
+                                  case.causal, case.scale, 0, 0, rows)
+        got = f64(out[b, h, rows])
+        worst = max(worst, check(got, ref, case.dtype, f"{case.name} seed={seed} b={b} h={h}"))
+    assert torch.isfinite(out).all()
+    return worst
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("case", W.DENSE_D128, ids=lambda c: c.name)
+def test_dense_d128_sampled(case, seed):
+    heads = [(0, 0), (case.B - 1, case.H - 1), (case.B // 2, 7)]
+    sampled_parity(case, seed, heads, nrows=48)
+
+
+@pytest.mark.parametrize("case", W.LONG, ids=lambda c: c.name)
+def test_long_sampled(case):
+    heads = [(0, 0), (0, 23), (0, 11)]
+    sampled_parity(case, 0, heads, nrows=32)
+
+
+@pytest.mark.parametrize("case", [c for c in W.GPT2_SWEEP if c.N == 4096], ids=lambda c: c.name)
+def test_gpt2_sweep_4096_sampled(case):
+    heads = [(0, 0), (case.B - 1, case.H - 1)]
+    sampled_parity(case, 2, heads, nrows=64)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1.0, 1e-3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_values(scale, causal):
+    full_parity(1, 2, 150, 64, "f16", causal, scale, seed=5)
+    full_parity(1, 2, 150, 128, "bf16", causal, scale, seed=6)
+
+
+def test_zero_query_gives_mean():
+    q, k, v = W.prefill_inputs(1, 2, 300, 128, "bf16", 3)
+    q = torch.zeros_like(q)
+    out = f64(run(q, k, v, False, 0.1))
+    ref = f64(v).mean(axis=2, keepdims=True) * np.ones_like(out)
+    check(out, ref, "bf16", "Q=0 mean")
+    outc = f64(run(q, k, v, True, 0.1))
+    refc = np.cumsum(f64(v), axis=2) / np.arange(1, 301)[None, None, :, None]
+    check(outc, refc, "bf16", "Q=0 prefix mean")
+
+
+def test_deterministic():
+    q, k, v = W.prefill_inputs(2, 4, 1000, 128, "bf16", 9)
+    a = run(q, k, v, True, 0.088)
+    b = run(q, k, v, True, 0.088)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causality_bit_identical(d):
+    """Rows 0..i are bit-identical when K/V rows after i change: the masked and
+    skipped tiles contribute exactly nothing."""
+    N, i = 700, 300
+    q, k, v = W.prefill_inputs(1, 2, N, d, "f16", 4)
+    a = run(q, k, v, True, 0.125)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i + 1:] = torch.randn(k2[:, :, i + 1:].shape).to(k2.dtype) * 3
+    v2[:, :, i + 1:] = 100.0
+    b = run(q, k2, v2, True, 0.125)
+    assert torch.equal(a[:, :, : i + 1].view(torch.int16), b[:, :, : i + 1].view(torch.int16))
+
+
+def test_output_canaries_and_nan_prefill():
+    B, H, N, d = 1, 3, 257, 128
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(B, H, N, d, "bf16", 8))
+    n = B * H * N * d
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    canary = torch.full((guard,), 12.5, dtype=torch.bfloat16, device=DEV)
+    buf[:guard] = canary
+    buf[-guard:] = canary
+    out = buf[guard:guard + n].view(B, H, N, d)
+    ea.prefill(q, k, v, causal=False, scale=0.0884, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:guard], canary) and torch.equal(buf[-guard:], canary)
+    assert torch.isfinite(out).all()
+
+
+def test_last_causal_row_matches_full():
+    q, k, v = W.prefill_inputs(1, 4, 999, 64, "f16", 10)
+    a = f64(run(q, k, v, False, 0.125))
+    b = f64(run(q, k, v, True, 0.125))
+    assert np.max(np.abs(a[:, :, -1] - b[:, :, -1])) <= 2e-3
+
+
+def test_python_errors():
+    q = torch.zeros(1, 1, 8, 96, dtype=torch.float16, device=DEV)
+    with pytest.raises(ValueError):
+        ea.prefill(q, q.clone(), q.clone())
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        ea.prefill(q, q.clone(), q.clone())
