@@ -4,23 +4,34 @@
 // the prompt-phase operation of the flash-attention-cuda README (page 3, "What can it
 // do" and "Kernel design"): K/V tiles are staged through on-chip memory, scores live
 // only in registers, a running row max m and row sum l in fp32 rescale the output
-// whenever the max moves (online softmax), and tiles wholly above the diagonal are
-// skipped by the loop bound.  Both contractions run on the matrix cores
+// when the max moves (online softmax), and tiles wholly above the diagonal are skipped
+// by the loop bound.  Both contractions run on the matrix cores
 // (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation), the step page 3 lists as
 // missing from its own kernel ("Limitations", "Future work").
 //
-// Work decomposition: one workgroup of 4 waves per (128-query block, head, batch).
-// Each wave owns 32 query rows.  The scores are computed transposed, S^T = K Q^T, so
-// that in the MFMA result layout every lane holds 16 scores of ONE query row: the
-// row max and row sum are in-lane reductions plus one exchange with the lane 32
-// apart, and the output rescale is a per-lane scalar.  The fp32 accumulator
-// registers of S^T are, after rounding to 16 bits, directly the B operand of the
-// second contraction O^T = V^T P^T.  That operand order needs V with the key index
-// along each lane's eight elements; V tiles are therefore written to LDS transposed
-// (d-major), with the key order permuted so each lane's eight keys are contiguous.
+// Work decomposition: one workgroup of 4 waves per (128-query block, head, batch);
+// each wave owns 32 query rows.  Scores are computed transposed, S^T = K Q^T, so that
+// in the MFMA result layout every lane holds 16 scores of ONE query row per 32-key
+// block: row max and row sum are in-lane reductions plus one exchange with the lane
+// 32 apart (v_permlane32_swap), and the output rescale is a per-lane scalar.  After
+// rounding to 16 bits, the S^T accumulator registers are directly the B operand of
+// the second contraction O^T = V^T P^T.
+//
+// Staging: K and V tiles go from HBM/L2 straight into LDS with buffer loads that
+// write LDS (no registers, no VALU), 16 bytes per lane, in row-major order with the
+// 16-byte chunks of each row XOR-swizzled by (row mod 8) so the MFMA operand reads
+// are free of bank conflicts.  V^T operands are read with the LDS transpose load
+// (ds_read_b64_tr_b16), which gathers four keys of one d column per lane.  Rows past
+// the end of the sequence fall outside the buffer's range and are not loaded.
+// Two LDS stages: tile j+1 is in flight while tile j is computed.
 //
 // Softmax runs in the base-2 domain: with c = scale*log2(e), p = 2^(c*s - m) where m
-// is the running max of c*s, which is the hardware exponential (v_exp_f32).
+// tracks the row max of c*s.  m is only raised when a new score exceeds it by more
+// than 2^8 (so p <= 256, harmless in fp32 accumulators and in fp16/bf16 P); most
+// tiles then skip the rescale of l and the output registers entirely.  The final
+// O = acc / l is unaffected, since acc and l always share the same m.
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -30,7 +41,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
-constexpr int VP = BN + 8;       // LDS pitch (elements) of one transposed V row
+constexpr float kLazyLog2 = 8.f;  // raise m only when a score exceeds it by > 2^8
 }  // namespace prefill_cfg
 
 struct PrefillParams {
@@ -45,27 +56,59 @@ struct PrefillParams {
   uint32_t qand;  // 0 zeroes Q (scale == 0), else 0xffffffff
 };
 
-// Position of key kk (0..63) of a tile inside a transposed V row: keys read together
-// by one lane for one MFMA step become 8 contiguous elements.  For the S^T result
-// layout, lane half h holds keys {8a + 4h + b} (a, b in 0..3) of each 32-key block.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int kb = kk >> 5, r = kk & 31;
-  const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
-  return 32 * kb + 16 * h + 4 * a + b;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* lds_base, uint32_t byte_off) {
+  const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)lds_base + byte_off));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(const uint16_t* lds_base, uint32_t byte_off) {
+  return *(const u32x4*)((const char*)lds_base + byte_off);
+}
+
+// max(x, x of the lane 32 apart) and the sum likewise, from one v_permlane32_swap:
+// it returns (x with its upper half replaced by the partner's lower half, and the
+// partner half's view), so the two results hold {x, partner} in some order.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row sum of packed 16-bit P pairs: sum += lo + hi (v_dot2 with (1, 1)).
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float add_pair<DT_BF16>(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                         acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<DT_F16>(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
 }
 
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(PrefillParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
   using namespace prefill_cfg;
-  constexpr int KP = D + 8;            // LDS pitch (elements) of one K row
-  constexpr int KS = D / 16;           // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;           // 32-wide output blocks along d
-  constexpr int KCH = BN * D / 8 / kThreads;  // 16-byte K chunks per thread per tile
-  constexpr int VUNITS = (BN / 4) * (D / 8);  // 4-key x 8-d transpose units per tile
-  constexpr int K_ELEMS = BN * KP;
-  constexpr int V_ELEMS = D * VP;
-  constexpr int STAGE = K_ELEMS + V_ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  constexpr int RB = D * 2;                  // bytes per K/V row
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;                 // 32-wide output blocks along d
+  constexpr int TILE_BYTES = BN * RB;        // one K (or V) tile
+  constexpr int NLD = TILE_BYTES / 1024 / kWaves;  // 1 KiB LDS-direct loads per wave per tile
+  constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // K tile then V tile
+  static_assert(NLD >= 1, "tile too small for the load pattern");
+  // One array per stage, so the compiler can tell the in-flight LDS-direct loads of
+  // one stage from the operand reads of the other and not wait on them.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE_BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -91,8 +134,8 @@ __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(Prefi
 
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t* __restrict__ qg = p.q + head_off;
-  const uint16_t* __restrict__ kg = p.k + head_off;
-  const uint16_t* __restrict__ vg = p.v + head_off;
+  const char* kbase = (const char*)(p.k + head_off);
+  const char* vbase = (const char*)(p.v + head_off);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8*half + 0..7].
   u32x4 qf[KS];
@@ -100,163 +143,177 @@ __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(Prefi
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 t = {0, 0, 0, 0};
     if (qrow < N) t = *(const u32x4*)(qg + (size_t)qrow * D + 16 * ks + 8 * half);
-    t = (t ^ p.qxor) & p.qand;
-    qf[ks] = t;
+    qf[ks] = (t ^ p.qxor) & p.qand;
+  }
+
+  // Per-lane byte offsets of the LDS-direct loads: load r of this wave fills LDS
+  // chunk ci = (wave*NLD + r)*64 + lane, i.e. row ci / (RB/16), physical slot
+  // ci % (RB/16), which holds logical 16-byte chunk slot ^ (row & 7).
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int r = 0; r < NLD; ++r) {
+    const int ci = (wave * NLD + r) * 64 + lane;
+    const int row = ci / (RB / 16), sl = ci % (RB / 16);
+    ld_off[r] = row * RB + ((sl ^ (row & 7)) << 4);
+  }
+  // K operand (A of S^T): row 32kb + l32, logical chunk 2ks + half.
+  uint32_t k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * RB + ((((2 * ks + half) ^ (l32 & 7))) << 4);
+  // V^T operand via transpose loads: in each 16-lane group, source lane r points at
+  // 4 consecutive d of key row (base + r/4), d0 = 32db + 16*((lane>>4)&1) + 4*(r&3).
+  uint32_t v_off[DB];
+  {
+    const int r = lane & 15, gg = (lane >> 4) & 1;
+    const int rowlo = 4 * half + (r >> 2);  // row within an 8-row group, = row & 7
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
+      v_off[db] = rowlo * RB + ((chunk ^ rowlo) << 4) + 8 * (r & 1);
+    }
   }
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;  // running max of c*s for this lane's query row
-  float l_run = 0.f;        // this lane's half of the running row sum
+  float m_run = -INFINITY;  // reference max of c*s for this lane's query row
+  float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
 
-  // ---- global -> register staging of one K/V tile ----
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  const int vc = tid & 15;   // 4-key group of the V unit
-  const int vdc = tid >> 4;  // 8-wide d chunk of the V unit
-  const bool vunit = tid < VUNITS;
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int ci = tid + r * kThreads;
-      const int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      u32x4 t = {0, 0, 0, 0};
-      if (k0 + row < N) t = *(const u32x4*)(kg + (size_t)(k0 + row) * D + col);
-      kreg[r] = t;
+  if (N % BN != 0) {
+    // The last tile is partial and its missing rows are never written: start from
+    // zeros so no uninitialised LDS bits can reach the MFMA (masked p is exactly 0).
+    for (int i = tid; i < STAGE_BYTES / 16; i += kThreads) {
+      ((u32x4*)lds0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)lds1)[i] = (u32x4){0, 0, 0, 0};
     }
-    if (vunit) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  auto issue_loads = [&](int k0, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const int rows_left = N - k0;
+    const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RB;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)k0 * RB), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)k0 * RB), 0, nrec, 0x00020000);
+    char* st = (char*)(stage == 0 ? lds0 : lds1);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int row = k0 + 4 * vc + b;
-        u32x4 t = {0, 0, 0, 0};
-        if (row < N) t = *(const u32x4*)(vg + (size_t)row * D + 8 * vdc);
-        vreg[b] = t;
-      }
+    for (int r = 0; r < NLD; ++r) {
+      char* dst = st + (wave * NLD + r) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)dst, 16, ld_off[r], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + TILE_BYTES), 16, ld_off[r], 0, 0, 0);
     }
   };
-
-  auto store_tile = [&](int stage) {
-    uint16_t* ks_ = lds + stage * STAGE;
-    uint16_t* vs_ = ks_ + K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int ci = tid + r * kThreads;
-      const int row = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      *(u32x4*)(ks_ + row * KP + col) = kreg[r];
-    }
-    if (vunit) {
-      // Transpose 4 keys x 8 d into 8 rows (one per d) of 4 consecutive keys.
-      const int pos = vt_pos(4 * vc);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const uint32_t w0 = vreg[0][x], w1 = vreg[1][x], w2 = vreg[2][x], w3 = vreg[3][x];
-        u32x2 lo, hi;
-        lo[0] = (w0 & 0xffffu) | (w1 << 16);
-        lo[1] = (w2 & 0xffffu) | (w3 << 16);
-        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-        *(u32x2*)(vs_ + (8 * vdc + 2 * x) * VP + pos) = lo;
-        *(u32x2*)(vs_ + (8 * vdc + 2 * x + 1) * VP + pos) = hi;
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
 
   const float c = p.c;
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * BN;
-    if (j + 1 < ntiles) load_tile(k0 + BN);
-
+  auto compute = [&](int k0, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const bool active = (qw0 < N) && (!CAUSAL || k0 <= qw0 + 31);
-    if (active) {
-      const uint16_t* ks_ = lds + (j & 1) * STAGE;
-      const uint16_t* vs_ = ks_ + K_ELEMS;
+    if (!active) return;
+    const uint16_t* ks_ = stage == 0 ? lds0 : lds1;
+    const uint16_t* vs_ = ks_ + TILE_BYTES / 2;
 
-      // S^T (keys x queries) for two 32-key blocks.
-      f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+    // S^T (keys x queries) for two 32-key blocks.
+    f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 kf = *(const u32x4*)(ks_ + (32 * kb + l32) * KP + 16 * ks + 8 * half);
-          sacc[kb] = mfma32x32x16<DT>(kf, qf[ks], sacc[kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = lds_read_b128(ks_, k_off[ks] + 32 * kb * RB);
+        sacc[kb] = mfma32x32x16<DT>(kf, qf[ks], sacc[kb]);
       }
+    }
 
-      // Mask keys past the end, and (causal) keys after the query row.
-      const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key > lim) sacc[kb][i] = -INFINITY;
-          }
-      }
-
-      float mx = -INFINITY;
+    // Mask keys past the end, and (causal) keys after the query row.
+    const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw0);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (key > lim) sacc[kb][i] = -INFINITY;
+        }
+    }
 
-      u32x4 pf[2][2];
-      float psum = 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+    mx = xhalf_max(mx);
+    const float cand = mx * c;
+    const bool raise = cand > m_run + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      // Only rows that need it move their m (alpha = 1 exactly elsewhere), so every
+      // row's arithmetic depends on its own scores alone.
+      const float alpha = raise ? fast_exp2(m_run - cand) : 1.f;  // m_run = -inf gives 0
+      m_run = raise ? cand : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+
+    u32x4 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 t;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][8 * s + 2 * x], c, neg_m));
+          const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * s + 2 * x + 1], c, neg_m));
+          t[x] = pack2<DT>(e0, e1);
+          l_run = add_pair<DT>(t[x], l_run);
+        }
+        pf[kb][s] = t;
+      }
+    }
+
+    // O^T (d x queries) += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          float e[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            e[jj] = fast_exp2(__builtin_fmaf(sacc[kb][8 * s + jj], c, neg_m));
-            psum += e[jj];
-          }
-          u32x4 t;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) t[x] = pack2<DT>(e[2 * x], e[2 * x + 1]);
-          pf[kb][s] = t;
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-      // O^T (d x queries) += V^T P^T.
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const u32x4 vf = *(const u32x4*)(vs_ + (32 * db + l32) * VP + 32 * kb + 16 * half + 8 * s);
-            oacc[db] = mfma32x32x16<DT>(vf, pf[kb][s], oacc[db]);
-          }
+          const uint32_t rowoff = (32 * kb + 16 * s) * RB;
+          const u32x2 lo = lds_read_tr(vs_, v_off[db] + rowoff);
+          const u32x2 hi = lds_read_tr(vs_, v_off[db] + rowoff + 8 * RB);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = mfma32x32x16<DT>(vf, pf[kb][s], oacc[db]);
         }
       }
     }
+  };
 
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  issue_loads(0, S0{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue_loads((j + 1) * BN, S1{});
+    compute(j * BN, S0{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue_loads((j + 2) * BN, S0{});
+    compute((j + 1) * BN, S1{});
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // Epilogue: O = acc / l.  Lane holds d = 32db + 8a + 4*half + b for a, b in 0..3.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   const float inv = 1.f / l_tot;
   if (qrow < N) {
     uint16_t* og = p.o + head_off + (size_t)qrow * D;
@@ -270,6 +327,7 @@ __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(Prefi
         *(u32x2*)(og + 32 * db + 8 * a + 4 * half) = t;
       }
   }
+#endif
 }
 
 template <int DT, int D, bool CAUSAL>
