@@ -4,7 +4,9 @@
 
 Compiles every kernel instance with hipcc for gfx950 only.  Packed fp32 vector
 instructions are switched off on purpose (-packed-fp32-ops): the compiler is free
-to form them from scalar float code otherwise.
+to form them from scalar float code otherwise.  NaN inputs are outside the
+library's contract, so IEEE NaN quieting is off (-fno-honor-nans,
+-mno-amdgpu-ieee); infinities keep their meaning.
 """
 
 from __future__ import annotations
@@ -29,6 +31,11 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Inputs are finite by contract (infinities are used internally for masking, NaNs
+    # never): without IEEE NaN quieting, fmax chains become v_max3 with no
+    # canonicalising moves in front of every operand.
+    "-fno-honor-nans",
+    "-mno-amdgpu-ieee",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

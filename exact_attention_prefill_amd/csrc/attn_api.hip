@@ -13,7 +13,7 @@
 
 namespace attn {
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int dt,
-                          int causal, float scale, hipStream_t s);
+                          int causal, float scale, int num_cus, hipStream_t s);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
                          int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws, hipStream_t st);
 }  // namespace attn
@@ -99,7 +99,9 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
     return st;
   if (out == q || out == k || out == v) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
-  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, N, d, dtype, causal, scale, (hipStream_t)stream);
+  int cus = 0;
+  if ((st = device_cus(&cus)) != ATTN_OK) return st;
+  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, N, d, dtype, causal, scale, cus, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -26,10 +26,12 @@
 // Two LDS stages: tile j+1 is in flight while tile j is computed.
 //
 // Softmax runs in the base-2 domain: with c = scale*log2(e), p = 2^(c*s - m) where m
-// tracks the row max of c*s.  m is only raised when a new score exceeds it by more
-// than 2^8 (so p <= 256, harmless in fp32 accumulators and in fp16/bf16 P); most
-// tiles then skip the rescale of l and the output registers entirely.  The final
-// O = acc / l is unaffected, since acc and l always share the same m.
+// is a reference for the row max of c*s.  P is computed with the current m without
+// waiting for the new scores' max; m is raised (and P redone, l and O rescaled) only
+// when a row's max exceeds it by more than 2^8, which a cheap guard on the sum of the
+// new p detects (p <= sum <= 4096 otherwise: harmless in fp32 accumulators and in
+// fp16/bf16 P).  The final O = acc / l is unaffected, since acc and l always share
+// the same m.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -37,11 +39,9 @@
 namespace attn {
 
 namespace prefill_cfg {
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
-constexpr float kLazyLog2 = 8.f;  // raise m only when a score exceeds it by > 2^8
+constexpr float kLazyLog2 = 8.f;     // raise m only when a score exceeds it by > 2^8
+constexpr float kSumGuard = 4096.f;  // a unit's per-lane sum of p above this prompts a check
 }  // namespace prefill_cfg
 
 struct PrefillParams {
@@ -50,7 +50,7 @@ struct PrefillParams {
   const uint16_t* v;
   uint16_t* o;
   int B, H, N;
-  int nqblk;      // ceil(N / BM)
+  int nqblk;      // ceil(N / BM), BM = 32 * waves per workgroup
   float c;        // |scale| * log2(e) (> 0); log2(e) when scale == 0
   uint32_t qxor;  // 0x80008000 flips Q's sign (scale < 0), else 0
   uint32_t qand;  // 0 zeroes Q (scale == 0), else 0xffffffff
@@ -94,24 +94,33 @@ __device__ __forceinline__ float add_pair<DT_F16>(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
 }
 
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(PrefillParams p) {
+// NW waves per workgroup, each owning QB blocks of 32 query rows.  QB = 1: two waves
+// share each SIMD (<= 256 registers).  QB = 2: the two row blocks share every K and V
+// operand read, halving LDS traffic per MFMA; a wave then needs ~350 registers, so
+// one wave runs per SIMD with the MFMA accumulators in AGPRs.
+template <int DT, int D, bool CAUSAL, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
   using namespace prefill_cfg;
-  constexpr int RB = D * 2;                  // bytes per K/V row
-  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;                 // 32-wide output blocks along d
-  constexpr int TILE_BYTES = BN * RB;        // one K (or V) tile
+  constexpr int kWaves = NW;
+  constexpr int kThreads = 64 * NW;
+  constexpr int QW = 32 * QB;                      // query rows per wave
+  constexpr int BM = QW * NW;                      // query rows per workgroup
+  constexpr int RB = D * 2;                        // bytes per K/V row
+  constexpr int KS = D / 16;                       // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;                       // 32-wide output blocks along d
+  constexpr int TILE_BYTES = BN * RB;              // one K (or V) tile
   constexpr int NLD = TILE_BYTES / 1024 / kWaves;  // 1 KiB LDS-direct loads per wave per tile
-  constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // K tile then V tile
   static_assert(NLD >= 1, "tile too small for the load pattern");
-  // One array per stage, so the compiler can tell the in-flight LDS-direct loads of
-  // one stage from the operand reads of the other and not wait on them.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE_BYTES / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE_BYTES / 2];
+  // Two K and two V tile buffers, each its own array so the compiler can tell the
+  // in-flight LDS-direct loads into one from the operand reads of another.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
@@ -124,13 +133,17 @@ __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(Prefi
   const int xcd = bid & 7, slot = bid >> 3;
   const int per = G >> 3, rem = G & 7;
   const int work = xcd * per + min(xcd, rem) + slot;
-  const int bh = work / p.nqblk;
-  int qb = work - bh * p.nqblk;
+  // Integer division is expanded on the VALU; pin the (uniform) results to SGPRs so
+  // the buffer descriptors built from them stay scalar.
+  const int bh = __builtin_amdgcn_readfirstlane(work / p.nqblk);
+  int qb = __builtin_amdgcn_readfirstlane(work - bh * p.nqblk);
   if (CAUSAL) qb = p.nqblk - 1 - qb;  // longest rows first
   const int N = p.N;
   const int q0 = qb * BM;
-  const int qw0 = q0 + 32 * wave;
-  const int qrow = qw0 + l32;
+  const int qw0 = q0 + QW * wave;
+  int qrow[QB];
+#pragma unroll
+  for (int cb = 0; cb < QB; ++cb) qrow[cb] = qw0 + 32 * cb + l32;
 
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t* __restrict__ qg = p.q + head_off;
@@ -138,207 +151,343 @@ __global__ __launch_bounds__(prefill_cfg::kThreads, 2) void prefill_kernel(Prefi
   const char* vbase = (const char*)(p.v + head_off);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8*half + 0..7].
-  u32x4 qf[KS];
+  u32x4 qf[QB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 t = {0, 0, 0, 0};
-    if (qrow < N) t = *(const u32x4*)(qg + (size_t)qrow * D + 16 * ks + 8 * half);
-    qf[ks] = (t ^ p.qxor) & p.qand;
-  }
+  for (int cb = 0; cb < QB; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 t = {0, 0, 0, 0};
+      if (qrow[cb] < N) t = *(const u32x4*)(qg + (size_t)qrow[cb] * D + 16 * ks + 8 * half);
+      qf[cb][ks] = (t ^ p.qxor) & p.qand;
+    }
 
-  // Per-lane byte offsets of the LDS-direct loads: load r of this wave fills LDS
-  // chunk ci = (wave*NLD + r)*64 + lane, i.e. row ci / (RB/16), physical slot
-  // ci % (RB/16), which holds logical 16-byte chunk slot ^ (row & 7).
-  uint32_t ld_off[NLD];
+  // Tile layout in LDS: row-major rows of RB bytes whose 16-byte chunks are permuted
+  // by XOR with a per-row key, chosen (by measurement) so that both operand reads are
+  // free of bank conflicts: the K reads (16 consecutive rows, one chunk each) and the
+  // V^T transpose reads (8 rows x 4 chunks).  K: row & 15 (d=128) or (row>>1) & 7
+  // (d=64); V: 2*(row & 7) (d=128) or row & 7 (d=64).
+  auto kkey = [](int row) __attribute__((always_inline)) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+  auto vkey = [](int row) __attribute__((always_inline)) { return D == 128 ? ((row & 7) << 1) : (row & 7); };
+  // LDS-direct load r of this wave fills LDS chunk ci = (wave*NLD + r)*64 + lane, i.e.
+  // row ci / (RB/16) and physical slot ci % (RB/16), which holds logical chunk
+  // slot ^ key(row): fetch that chunk from memory.
+  uint32_t ldk_off[NLD], ldv_off[NLD];
 #pragma unroll
   for (int r = 0; r < NLD; ++r) {
     const int ci = (wave * NLD + r) * 64 + lane;
     const int row = ci / (RB / 16), sl = ci % (RB / 16);
-    ld_off[r] = row * RB + ((sl ^ (row & 7)) << 4);
+    ldk_off[r] = row * RB + ((sl ^ kkey(row)) << 4);
+    ldv_off[r] = row * RB + ((sl ^ vkey(row)) << 4);
   }
-  // K operand (A of S^T): row 32kb + l32, logical chunk 2ks + half.
+  // K operand (A of S^T): row 32kb + l32 (key(row) does not depend on kb), logical
+  // chunk 2ks + half.
   uint32_t k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * RB + ((((2 * ks + half) ^ (l32 & 7))) << 4);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * RB + (((2 * ks + half) ^ kkey(l32)) << 4);
   // V^T operand via transpose loads: in each 16-lane group, source lane r points at
-  // 4 consecutive d of key row (base + r/4), d0 = 32db + 16*((lane>>4)&1) + 4*(r&3).
+  // 4 consecutive d of key row (base + r/4), d0 = 32db + 16*((lane>>4)&1) + 4*(r&3);
+  // base is a multiple of 8, so key(row) = key(row & 7).
   uint32_t v_off[DB];
   {
     const int r = lane & 15, gg = (lane >> 4) & 1;
-    const int rowlo = 4 * half + (r >> 2);  // row within an 8-row group, = row & 7
+    const int rowlo = 4 * half + (r >> 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
-      v_off[db] = rowlo * RB + ((chunk ^ rowlo) << 4) + 8 * (r & 1);
+      v_off[db] = rowlo * RB + ((chunk ^ vkey(rowlo)) << 4) + 8 * (r & 1);
     }
   }
 
-  f32x16 oacc[DB];
+  f32x16 oacc[QB][DB];
+  float m_run[QB];  // reference max of c*s for this lane's query row
+  float neg_m[QB];  // -m_run, kept beside it (m_run is finite once unit 0 is seen)
+  float l_run[QB];  // this lane's half of the row sum, relative to m_run
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;  // reference max of c*s for this lane's query row
-  float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
+  for (int cb = 0; cb < QB; ++cb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[cb][db] = (f32x16){};
+    m_run[cb] = -INFINITY;
+    neg_m[cb] = 0.f;
+    l_run[cb] = 0.f;
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int nt = (kv_end + BN - 1) / BN;  // 64-key tiles this workgroup stages
+  const int nu = (kv_end + 31) / 32;      // 32-key units in those tiles
+  // Units this wave computes: a prefix (causal waves stop at their diagonal).
+  const int nu_w = qw0 >= N ? 0 : (CAUSAL ? min(nu, (qw0 + QW - 1) / 32 + 1) : nu);
 
   if (N % BN != 0) {
     // The last tile is partial and its missing rows are never written: start from
     // zeros so no uninitialised LDS bits can reach the MFMA (masked p is exactly 0).
-    for (int i = tid; i < STAGE_BYTES / 16; i += kThreads) {
-      ((u32x4*)lds0)[i] = (u32x4){0, 0, 0, 0};
-      ((u32x4*)lds1)[i] = (u32x4){0, 0, 0, 0};
+    for (int i = tid; i < TILE_BYTES / 16; i += kThreads) {
+      ((u32x4*)kbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)kbuf1)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf1)[i] = (u32x4){0, 0, 0, 0};
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  auto issue_loads = [&](int k0, auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
+  auto load_tile = [&](const char* src_base, const uint32_t (&offs)[NLD], int t, char* dst) __attribute__((always_inline)) {
+    const int k0 = t * BN;
     const int rows_left = N - k0;
     const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RB;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)k0 * RB), 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)k0 * RB), 0, nrec, 0x00020000);
-    char* st = (char*)(stage == 0 ? lds0 : lds1);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src_base + (size_t)k0 * RB), 0, nrec, 0x00020000);
 #pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      char* dst = st + (wave * NLD + r) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)dst, 16, ld_off[r], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(dst + TILE_BYTES), 16, ld_off[r], 0, 0, 0);
-    }
+    for (int i = 0; i < NLD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * NLD + i) * 1024), 16, offs[i], 0, 0, 0);
   };
+  auto load_k = [&](int t, char* dst) __attribute__((always_inline)) { load_tile(kbase, ldk_off, t, dst); };
+  auto load_v = [&](int t, char* dst) __attribute__((always_inline)) { load_tile(vbase, ldv_off, t, dst); };
 
-  const float c = p.c;
-  auto compute = [&](int k0, auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const bool active = (qw0 < N) && (!CAUSAL || k0 <= qw0 + 31);
-    if (!active) return;
-    const uint16_t* ks_ = stage == 0 ? lds0 : lds1;
-    const uint16_t* vs_ = ks_ + TILE_BYTES / 2;
-
-    // S^T (keys x queries) for two 32-key blocks.
-    f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+  // ---- per-unit pieces (a unit is 32 keys: one half of a staged 64-key tile) ----
+  // Operand of score MFMA ks for the unit in half h of a K tile.
+  auto kread = [&](const char* kb_, int h, int ks) __attribute__((always_inline)) {
+    return lds_read_b128((const uint16_t*)kb_, k_off[ks] + 32 * h * RB);
+  };
+  // V^T operand of P*V MFMA (s, db) for the unit in half h of a V tile.
+  auto vread = [&](const char* vb_, int h, int s, int db) __attribute__((always_inline)) {
+    const uint32_t off = v_off[db] + (32 * h + 16 * s) * RB;
+    const u32x2 lo = lds_read_tr((const uint16_t*)vb_, off);
+    const u32x2 hi = lds_read_tr((const uint16_t*)vb_, off + 8 * RB);
+    return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  };
+  // Keys past the end, and (causal) keys after the query row, score -inf.
+  auto mask_unit = [&](f32x16& sc, int u, int cb) __attribute__((always_inline)) {
+    const int k0 = 32 * u;
+    const bool need = (k0 + 32 > N) || (CAUSAL && k0 + 31 > qw0 + 32 * cb);
+    if (need) {
+      const int lim = CAUSAL ? min(qrow[cb], N - 1) : N - 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 kf = lds_read_b128(ks_, k_off[ks] + 32 * kb * RB);
-        sacc[kb] = mfma32x32x16<DT>(kf, qf[ks], sacc[kb]);
-      }
-    }
-
-    // Mask keys past the end, and (causal) keys after the query row.
-    const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw0);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key > lim) sacc[kb][i] = -INFINITY;
-        }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
-    mx = xhalf_max(mx);
-    const float cand = mx * c;
-    const bool raise = cand > m_run + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      // Only rows that need it move their m (alpha = 1 exactly elsewhere), so every
-      // row's arithmetic depends on its own scores alone.
-      const float alpha = raise ? fast_exp2(m_run - cand) : 1.f;  // m_run = -inf gives 0
-      m_run = raise ? cand : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 t;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][8 * s + 2 * x], c, neg_m));
-          const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][8 * s + 2 * x + 1], c, neg_m));
-          t[x] = pack2<DT>(e0, e1);
-          l_run = add_pair<DT>(t[x], l_run);
-        }
-        pf[kb][s] = t;
-      }
-    }
-
-    // O^T (d x queries) += V^T P^T.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint32_t rowoff = (32 * kb + 16 * s) * RB;
-          const u32x2 lo = lds_read_tr(vs_, v_off[db] + rowoff);
-          const u32x2 hi = lds_read_tr(vs_, v_off[db] + rowoff + 8 * RB);
-          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = mfma32x32x16<DT>(vf, pf[kb][s], oacc[db]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (key > lim) sc[i] = -INFINITY;
       }
     }
   };
+  // Row max of a unit (in-lane over 16 scores, then across the two lane halves).
+  auto unit_max = [&](const f32x16& sc) __attribute__((always_inline)) {
+    float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[i], sc[i + 1]));
+    return xhalf_max(mx);
+  };
+  // P dword w (of 8) of a unit, in three steps that the schedule spreads over
+  // consecutive issue slots: x = c s - m (two FMAs), e = 2^x, then round to 16 bits,
+  // pack and add into the unit's row sum.
+  auto p_arg = [&](const f32x16& sc, float nm, int w, float (&x)[2]) __attribute__((always_inline)) {
+    x[0] = __builtin_fmaf(sc[2 * w], p.c, nm);
+    x[1] = __builtin_fmaf(sc[2 * w + 1], p.c, nm);
+  };
+  auto p_exp = [&](float (&x)[2]) __attribute__((always_inline)) {
+    x[0] = fast_exp2(x[0]);
+    x[1] = fast_exp2(x[1]);
+  };
+  auto p_pack = [&](const float (&e)[2], u32x4 (&pf)[2], float& l_unit, int w) __attribute__((always_inline)) {
+    const uint32_t t = pack2<DT>(e[0], e[1]);
+    pf[w >> 2][w & 3] = t;
+    l_unit = add_pair<DT>(t, l_unit);
+  };
+  // All of a unit's P with the given -m (the slow path and the prologue).
+  auto p_all = [&](const f32x16& sc, u32x4 (&pf)[2], float& l_unit, float nm) __attribute__((always_inline)) {
+    l_unit = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float x[2];
+      p_arg(sc, nm, w, x);
+      p_exp(x);
+      p_pack(x, pf, l_unit, w);
+    }
+  };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  issue_loads(0, S0{});
+  // One pipeline iteration u of this wave, a three-stage pipeline over units:
+  //   matrix cores: S_{u+2} = K_{u+2} Q^T  interleaved with  O += V_u^T P_u;
+  //   VALU:         P_{u+1} = 2^(c S_{u+1} - m).
+  // P_{u+1} is computed optimistically with the current m.  Every p of a lane is at
+  // most the lane's sum of the unit, so a sum within kSumGuard means no p left the
+  // safe range and m may stay; otherwise the real row max decides: rows whose max
+  // exceeds m by more than 2^8 raise m (alpha = 1 exactly elsewhere, so each row
+  // depends on its own scores alone), P_{u+1} is recomputed and l and O rescaled (O
+  // after this iteration's MFMAs into it).  The softmax is spread over all the
+  // iteration's MFMAs, about three VALU instructions (one exponential) per MFMA, with
+  // each dependent step in a later slot than its input.
+  // scur = S_{u+1} (scored last iteration), snext receives S_{u+2}; pcur = P_u,
+  // pnext receives P_{u+1}.  kb_/h_k locate K of unit u+2, vb_/h_v V of unit u.
+  // Near the end of a wave's range S_{u+2} may score keys it never uses: such a unit
+  // is fully masked when it is consumed, so m and l do not move and P is zero.
+  // Eight issue slots per iteration.  d = 128: slot i issues score MFMA i and P*V MFMA
+  // i (s = i/4, db = i%4).  d = 64 (4 + 4 MFMAs): even slots score, odd slots P*V.
+  // Each K or V operand read feeds the MFMAs of all QB row blocks.
+  constexpr int NP = 2 * DB;  // P*V MFMAs per unit and row block
+  constexpr int PF = 2;       // operand prefetch distance (MFMAs of the same kind)
+  auto s_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 0 ? i >> 1 : -1); };
+  auto p_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 1 ? i >> 1 : -1); };
+  auto iterate = [&](int u, f32x16 (&scur)[QB], f32x16 (&snext)[QB], const u32x4 (&pcur)[QB][2],
+                     u32x4 (&pnext)[QB][2], const char* kb_, int h_k, const char* vb_, int h_v) __attribute__((always_inline)) {
+    float l_unit[QB];
+    float xa[QB][2], xb[QB][2];  // P arguments / exponentials in flight, two dwords apart
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) {
+      mask_unit(scur[cb], u + 1, cb);  // a unit past this wave's keys masks entirely: p = 0
+      l_unit[cb] = 0.f;
+    }
+    u32x4 kf[PF + 1], vf[PF + 1];
+#pragma unroll
+    for (int a = 0; a < PF; ++a) {
+      kf[a] = kread(kb_, h_k, a);
+      vf[a] = vread(vb_, h_v, a / DB, a % DB);
+    }
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) p_arg(scur[cb], neg_m[cb], 0, xa[cb]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int a = s_at(i), b = p_at(i);
+      if (a >= 0) {
+        if (a + PF < KS) kf[(a + PF) % (PF + 1)] = kread(kb_, h_k, a + PF);
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb)  // the first MFMA of a chain takes a literal zero addend
+          snext[cb] = mfma32x32x16<DT>(kf[a % (PF + 1)], qf[cb][a], a == 0 ? (f32x16){} : snext[cb]);
+      }
+      if (b >= 0) {
+        if (b + PF < NP) vf[(b + PF) % (PF + 1)] = vread(vb_, h_v, (b + PF) / DB, (b + PF) % DB);
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb)
+          oacc[cb][b % DB] = mfma32x32x16<DT>(vf[b % (PF + 1)], pcur[cb][b / DB], oacc[cb][b % DB]);
+      }
+      // slot i: exponentials of dword i, pack of dword i-1, arguments of dword i+1
+#pragma unroll
+      for (int cb = 0; cb < QB; ++cb) {
+        float (&cur_x)[2] = (i & 1) ? xb[cb] : xa[cb];
+        float (&oth_x)[2] = (i & 1) ? xa[cb] : xb[cb];
+        p_exp(cur_x);
+        if (i >= 1) p_pack(oth_x, pnext[cb], l_unit[cb], i - 1);
+        if (i + 1 < 8) p_arg(scur[cb], neg_m[cb], i + 1, oth_x);
+        // Anchor this slot's VALU results in the slot: IR-level code motion ignores
+        // sched_barrier and would otherwise gather the softmax after the MFMAs.
+        asm volatile("" ::"v"(cur_x[0]), "v"(cur_x[1]), "v"(oth_x[0]), "v"(oth_x[1]), "v"(l_unit[cb]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bool over = false;
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) {
+      p_pack((7 & 1) ? xb[cb] : xa[cb], pnext[cb], l_unit[cb], 7);
+      over = over || (l_unit[cb] > kSumGuard);
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < QB; ++cb) {
+        const float cand = unit_max(scur[cb]) * p.c;
+        const bool raise = cand > m_run[cb] + kLazyLog2;
+        const float alpha = raise ? fast_exp2(m_run[cb] - cand) : 1.f;
+        m_run[cb] = raise ? cand : m_run[cb];
+        neg_m[cb] = -m_run[cb];
+        p_all(scur[cb], pnext[cb], l_unit[cb], neg_m[cb]);
+        l_run[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[cb][db] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) l_run[cb] += l_unit[cb];
+  };
+
+  // Prologue: K_0, V_0, K_1 in; S_0 and S_1; P_0; then V_1 and K_2 in flight.
+  f32x16 sx[QB], sy[QB];
+  u32x4 pa[QB][2], pb[QB][2];
+  load_k(0, kbuf0);
+  load_v(0, vbuf0);
+  if (nt > 1) load_k(1, kbuf1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue_loads((j + 1) * BN, S1{});
-    compute(j * BN, S0{});
+  if (nu_w > 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 k0f = kread(kbuf0, 0, ks), k1f = kread(kbuf0, 1, ks);
+#pragma unroll
+      for (int cb = 0; cb < QB; ++cb) {
+        sx[cb] = mfma32x32x16<DT>(k0f, qf[cb][ks], ks == 0 ? (f32x16){} : sx[cb]);
+        sy[cb] = mfma32x32x16<DT>(k1f, qf[cb][ks], ks == 0 ? (f32x16){} : sy[cb]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) {
+      mask_unit(sx[cb], 0, cb);
+      m_run[cb] = unit_max(sx[cb]) * p.c;  // key 0 is always visible, so this is finite
+      neg_m[cb] = -m_run[cb];
+      p_all(sx[cb], pa[cb], l_run[cb], neg_m[cb]);
+    }
+  }
+  __syncthreads();
+  if (nt > 1) load_v(1, vbuf1);
+  if (nt > 2) load_k(2, kbuf0);
+
+  // Tile t: units 2t, 2t+1 use V_t (vbuf[t&1]) and score units 2t+2, 2t+3 from
+  // K_{t+1} (kbuf[(t+1)&1]).  After the tile, V_{t+2} and K_{t+3} take the buffers
+  // just read.  Every wave passes the same nt barriers; a wave computes units
+  // u < nu_w only.  Scores of units past nu_w (or of tiles never staged) are
+  // computed but only ever consumed fully masked.
+  auto sync_and_load = [&](int t, char* kb_next, char* vb_cur) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue_loads((j + 2) * BN, S0{});
-    compute((j + 1) * BN, S1{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (t + 2 < nt) load_v(t + 2, vb_cur);
+    if (t + 3 < nt) load_k(t + 3, kb_next);
+  };
+  auto tile = [&](int t, char* kb_next, char* vb_cur) __attribute__((always_inline)) {
+    if (2 * t < nu_w) iterate(2 * t, sy, sx, pa, pb, kb_next, 0, vb_cur, 0);
+    if (2 * t + 1 < nu_w) iterate(2 * t + 1, sx, sy, pb, pa, kb_next, 1, vb_cur, 1);
+    sync_and_load(t, kb_next, vb_cur);
+  };
+  for (int t = 0; t < nt; t += 2) {
+    tile(t, kbuf1, vbuf0);
+    if (t + 1 < nt) tile(t + 1, kbuf0, vbuf1);
   }
 
   // Epilogue: O = acc / l.  Lane holds d = 32db + 8a + 4*half + b for a, b in 0..3.
-  const float l_tot = xhalf_sum(l_run);
-  const float inv = 1.f / l_tot;
-  if (qrow < N) {
-    uint16_t* og = p.o + head_off + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int cb = 0; cb < QB; ++cb) {
+    const float l_tot = xhalf_sum(l_run[cb]);
+    const float inv = 1.f / l_tot;
+    if (qrow[cb] < N) {
+      uint16_t* og = p.o + head_off + (size_t)qrow[cb] * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 t;
-        t[0] = pack2<DT>(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv);
-        t[1] = pack2<DT>(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
-        *(u32x2*)(og + 32 * db + 8 * a + 4 * half) = t;
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 t;
+          t[0] = pack2<DT>(oacc[cb][db][4 * a + 0] * inv, oacc[cb][db][4 * a + 1] * inv);
+          t[1] = pack2<DT>(oacc[cb][db][4 * a + 2] * inv, oacc[cb][db][4 * a + 3] * inv);
+          *(u32x2*)(og + 32 * db + 8 * a + 4 * half) = t;
+        }
+    }
   }
 #endif
 }
 
-template <int DT, int D, bool CAUSAL>
-static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+template <int DT, int D, bool CAUSAL, int NW, int QB>
+static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
+  constexpr int BM = 32 * QB * NW;
+  p.nqblk = (p.N + BM - 1) / BM;
   const long long grid = (long long)p.nqblk * p.H * p.B;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL>), dim3((unsigned)grid), dim3(prefill_cfg::kThreads), 0, s, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL, NW, QB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
+template <int DT, int D, bool CAUSAL>
+static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStream_t s) {
+  // Four waves of 32 query rows, two workgroups per CU (two waves per SIMD).  The
+  // 64-row form (QB = 2) halves LDS operand traffic per MFMA but, at one wave per
+  // SIMD with its score accumulators in AGPRs, measured slower on the d = 128 bf16
+  // 16K-token shape (0.98 vs 1.10 PFLOP/s), so it is not selected.
+  (void)num_cus;
+  return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
+}
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int dt,
-                          int causal, float scale, hipStream_t s) {
+                          int causal, float scale, int num_cus, hipStream_t s) {
   PrefillParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -347,7 +496,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   p.B = B;
   p.H = H;
   p.N = N;
-  p.nqblk = (N + prefill_cfg::BM - 1) / prefill_cfg::BM;
+  p.nqblk = 0;
   // Scores use c = |scale| log2(e) > 0 so the running max is a max of c*s; a negative
   // scale is carried by flipping Q's sign bits, a zero scale by a zero Q (all scores 0).
   const float as = scale < 0 ? -scale : scale;
@@ -355,7 +504,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   p.qxor = scale < 0 ? 0x80008000u : 0u;
   p.qand = scale == 0.f ? 0u : 0xffffffffu;
 #define ATTN_PF(DT_, D_, C_) \
-  if (dt == DT_ && d == D_ && causal == C_) return launch_prefill_t<DT_, D_, C_>(p, s);
+  if (dt == DT_ && d == D_ && causal == C_) return launch_prefill_w<DT_, D_, C_>(p, num_cus, s);
   ATTN_PF(DT_F16, 64, false)
   ATTN_PF(DT_F16, 64, true)
   ATTN_PF(DT_F16, 128, false)
