@@ -15,7 +15,7 @@ Prints ONE JSON line.  `value` is prefill TFLOP/s over the whole timed region
 (algorithmic flop 4*B*H*N*N*d per step / wall time per step, decode included in the
 time).  `roofline` covers the prefill kernel, timed with HIP events on the stream it
 runs on.  `decode` reports the decode path's HBM rate, timed with events after a
-512 MiB write that evicts the L2 and the Infinity Cache before every call.
+512 MiB read that evicts the L2 and the Infinity Cache before every call.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
 """
 
@@ -181,11 +181,14 @@ def main():
     value = P.flop / (ms_per_step * 1e-3) / 1e12
     log(f"prefill {pre_mean:.3f} ms/launch = {pre_tflops:.1f} TFLOP/s; step {ms_per_step:.3f} ms")
 
-    # Decode, cold: evict L2 and the 256 MB Infinity Cache with a 512 MiB write first.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Decode, cold: evict L2 and the 256 MB Infinity Cache by reading 512 MiB first.
+    # A read leaves clean lines behind; a write-based flush would leave ~256 MB of
+    # dirty lines whose write-back then competes with the decode's reads.
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
     cold = []
     for i in range(args.decode_iters):
-        flush.zero_()
+        torch.sum(flush, dim=0, out=flush_sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         ea.decode(dq_, dk_, dv_, dl_, scale=D.scale, out=dout, chunk=chunk, workspace=ws)

@@ -8,23 +8,25 @@
 //
 // The split kernel is a streaming read of K and V rows: arithmetic intensity is about
 // one flop per byte, so it is bound by HBM, not by the matrix cores, and runs on the
-// vector ALUs.  A row of the cache (d 16-bit values) is read by d/8 lanes with one
-// 16-byte load each, so one wave-wide load covers consecutive rows in one contiguous
-// kilobyte.  Four row-groups per lane are loaded before any is used to keep enough
-// bytes in flight.  Scores are kept in the base-2 domain (c = scale*log2(e)).
+// vector ALUs.  One wave owns one chunk.  A cache row (d 16-bit values) is read by d/8
+// lanes with one 16-byte load each, so one wave-wide load covers consecutive rows in
+// one contiguous kilobyte; two iterations of four such loads of K and of V are in
+// flight per lane.  The wave's row groups are combined with cross-lane exchanges,
+// so the kernel needs neither LDS nor barriers and many chunk-waves share a CU.
+// Scores are kept in the base-2 domain (c = scale*log2(e)).
 //
 // Partial layout in the workspace, for pair = b*H + h and split s:
 //   acc[(pair*n_split + s)*d + 0 .. d-1]  sum_t 2^(c s_t - m) v_t       (fp32)
 //   ml [(pair*n_split + s)*2 + 0, 1]      m = max_t c s_t, l = sum_t 2^(c s_t - m)
-// where acc is the first B*H*n_split*d floats and ml follows it.
+// where acc is the first B*H*n_split*d floats and ml follows it.  A chunk at or past
+// the sequence's length writes only (m, l) = (-inf, 0); its acc is never read.
 #include "attn_device.h"
 
 namespace attn {
 
 namespace decode_cfg {
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kGranule = 32;  // legal chunks are multiples of this many rows
+constexpr int kUnroll = 4;          // row loads of K (and of V) per lane per buffer (two buffers)
+constexpr int kMergeThreads = 256;  // merge workgroup: 4 split groups x 64
 }  // namespace decode_cfg
 
 struct DecodeParams {
@@ -41,27 +43,39 @@ struct DecodeParams {
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
 
+// Combine two online-softmax states (m, l, acc[8]) exactly: the larger m wins and the
+// other side is scaled by 2^(m_other - m).  m = -inf means empty.
+__device__ __forceinline__ void combine(float& m, float& l, float (&acc)[8], float m2, float l2, const float (&acc2)[8]) {
+  const float mn = fmaxf(m, m2);
+  const float a = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+  const float b = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mn);
+  m = mn;
+  l = l * a + l2 * b;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) acc[x] = acc[x] * a + acc2[x] * b;
+}
+
 template <int DT, int D>
-__global__ __launch_bounds__(decode_cfg::kThreads) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_split_kernel(DecodeParams p) {
   using namespace decode_cfg;
-  constexpr int LPR = D / 8;             // lanes per cache row
-  constexpr int RPW = 64 / LPR;          // rows per wave per load
-  constexpr int NW = kThreads / 64;      // waves
-  constexpr int RSTEP = NW * RPW;        // rows per workgroup per load
-  constexpr int RITER = RSTEP * kUnroll;  // rows per loop iteration
-  constexpr int NG = NW * RPW;           // independent row groups per workgroup
+  constexpr int LPR = D / 8;      // lanes per cache row
+  constexpr int RPW = 64 / LPR;   // rows per wave-wide load
+  constexpr int RITER = RPW * kUnroll;
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = clamp_len(p.seq_lens[b], p.max_len);
   const int r0 = s * p.chunk;
-  if (r0 >= L) return;  // empty chunk: the merge pass never reads it
+  const int lane = threadIdx.x;
+  const size_t pair = (size_t)b * p.H + h;
+  const size_t pidx = pair * p.n_split + s;
+  if (r0 >= L) {  // empty chunk: mark it so the merge needs no lengths
+    if (lane == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(-INFINITY, 0.f);
+    return;
+  }
   const int r1 = min(L, r0 + p.chunk);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int seg = lane % LPR;       // which 8 elements of d
-  const int rsub = lane / LPR;      // row within the wave's load
-  const int grp = wave * RPW + rsub;  // row group id (0 .. NG-1)
-  const size_t pair = (size_t)b * p.H + h;
+  const int seg = lane % LPR;   // which 8 elements of d
+  const int rsub = lane / LPR;  // row within one wave-wide load
   const uint16_t* kg = p.k + pair * p.max_len * D + seg * 8;
   const uint16_t* vg = p.v + pair * p.max_len * D + seg * 8;
 
@@ -79,19 +93,21 @@ __global__ __launch_bounds__(decode_cfg::kThreads) void decode_split_kernel(Deco
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = 0.f;
 
-  for (int base = r0; base < r1; base += RITER) {
-    u32x4 kr[kUnroll], vr[kUnroll];
-    int rows[kUnroll];
+  // Rows of one iteration: base + u*RPW + rsub.  The loads of iteration i+1 are
+  // issued before iteration i is reduced, so a wave keeps two iterations in flight.
+  auto load = [&](int base, u32x4 (&kr)[kUnroll], u32x4 (&vr)[kUnroll]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      rows[u] = base + u * RSTEP + grp;
+      const int row = base + u * RPW + rsub;
       kr[u] = (u32x4){0, 0, 0, 0};
       vr[u] = (u32x4){0, 0, 0, 0};
-      if (rows[u] < r1) {
-        kr[u] = *(const u32x4*)(kg + (size_t)rows[u] * D);
-        vr[u] = *(const u32x4*)(vg + (size_t)rows[u] * D);
+      if (row < r1) {
+        kr[u] = *(const u32x4*)(kg + (size_t)row * D);
+        vr[u] = *(const u32x4*)(vg + (size_t)row * D);
       }
     }
+  };
+  auto reduce = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll]) __attribute__((always_inline)) {
     float sc[kUnroll];
     float mx = m;
 #pragma unroll
@@ -105,91 +121,146 @@ __global__ __launch_bounds__(decode_cfg::kThreads) void decode_split_kernel(Deco
       // Sum the LPR lanes of this row (aligned groups of LPR consecutive lanes).
 #pragma unroll
       for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off);
-      sc[u] = rows[u] < r1 ? part : -INFINITY;
+      sc[u] = base + u * RPW + rsub < r1 ? part : -INFINITY;
       mx = fmaxf(mx, sc[u]);
     }
-    if (mx == -INFINITY) continue;  // nothing valid for this group in this iteration
-    const float alpha = fast_exp2(m - mx);  // m = -inf gives 0
-    m = mx;
-    l *= alpha;
+    if (mx != -INFINITY) {  // this row group has valid rows in this iteration
+      const float alpha = fast_exp2(m - mx);  // m = -inf gives 0
+      m = mx;
+      l *= alpha;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+      for (int x = 0; x < 8; ++x) acc[x] *= alpha;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float pu = fast_exp2(sc[u] - m);  // -inf gives 0
-      l += pu;
+      for (int u = 0; u < kUnroll; ++u) {
+        const float pu = fast_exp2(sc[u] - m);  // -inf gives 0
+        l += pu;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        acc[2 * x] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] & 0xffffu), acc[2 * x]);
-        acc[2 * x + 1] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] >> 16), acc[2 * x + 1]);
+        for (int x = 0; x < 4; ++x) {
+          acc[2 * x] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] & 0xffffu), acc[2 * x]);
+          acc[2 * x + 1] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] >> 16), acc[2 * x + 1]);
+        }
       }
     }
+  };
+  u32x4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+  load(r0, ka, va);
+  for (int base = r0; base < r1; base += 2 * RITER) {
+    if (base + RITER < r1) load(base + RITER, kb, vb);
+    reduce(base, ka, va);
+    if (base + RITER >= r1) break;
+    if (base + 2 * RITER < r1) load(base + 2 * RITER, ka, va);
+    reduce(base + RITER, kb, vb);
   }
 
-  // Merge the NG row groups of this workgroup through LDS.
-  __shared__ float sm_m[NG], sm_l[NG], sm_w[NG];
-  __shared__ float sm_acc[NG][D + 1];
-  if (seg == 0) {
-    sm_m[grp] = m;
-    sm_l[grp] = l;
-  }
+  // Combine the RPW row groups of the wave (lanes rsub*LPR + seg) pairwise.
 #pragma unroll
-  for (int x = 0; x < 8; ++x) sm_acc[grp][seg * 8 + x] = acc[x];
-  __syncthreads();
-  __shared__ float sm_M;
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int g = 0; g < NG; ++g) M = fmaxf(M, sm_m[g]);
-    sm_M = M;
+  for (int off = LPR; off < 64; off <<= 1) {
+    float acc2[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc2[x] = __shfl_xor(acc[x], off);
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    combine(m, l, acc, m2, l2, acc2);
   }
-  __syncthreads();
-  const float M = sm_M;
-  if (tid < NG) sm_w[tid] = (sm_m[tid] == -INFINITY) ? 0.f : fast_exp2(sm_m[tid] - M);
-  __syncthreads();
-  const size_t pidx = pair * p.n_split + s;
-  if (tid < D) {
-    float a = 0.f;
-    for (int g = 0; g < NG; ++g) a = __builtin_fmaf(sm_w[g], sm_acc[g][tid], a);
-    p.ws_acc[pidx * D + tid] = a;
-  }
-  if (tid == 0) {
-    float lt = 0.f;
-    for (int g = 0; g < NG; ++g) lt = __builtin_fmaf(sm_w[g], sm_l[g], lt);
-    p.ws_ml[pidx * 2 + 0] = M;
-    p.ws_ml[pidx * 2 + 1] = lt;
+  if (rsub == 0) {
+    float* out = p.ws_acc + pidx * D + seg * 8;
+    *(f32x4*)out = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(out + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]};
+    if (seg == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(m, l);
   }
 }
 
 // Exact merge: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the non-empty
-// splits s < ceil(L / chunk); a length of 0 writes zeros.
+// splits (empty ones carry m = -inf); a length of 0 writes zeros.  Four groups of 64
+// threads take every fourth split, eight splits per round, each round's loads issued
+// together (one memory latency per round rather than per split).  The groups' sums
+// meet in LDS in a fixed order, so the result is deterministic.
 template <int DT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+  using namespace decode_cfg;
+  constexpr int NG = kMergeThreads / 64;
+  constexpr int DPT = D / 64;  // d elements per thread
+  constexpr int NBAT = 8;      // splits per group per round
+  __shared__ float sm_M[NG];
+  __shared__ float sm_den[NG];
+  __shared__ float sm_num[NG][D];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, g = t >> 6, lane = t & 63;
   const size_t pair = (size_t)b * p.H + h;
-  const int L = clamp_len(p.seq_lens[b], p.max_len);
-  const int nv = (L + p.chunk - 1) / p.chunk;
+  const int nv = p.n_split;  // empty chunks carry m = -inf and weigh nothing
   const float* ml = p.ws_ml + pair * p.n_split * 2;
   const float* ac = p.ws_acc + pair * p.n_split * D;
-  float M = -INFINITY;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[2 * s]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < nv; ++s) {
-    const float w = fast_exp2(ml[2 * s] - M);
-    den = __builtin_fmaf(w, ml[2 * s + 1], den);
-    num = __builtin_fmaf(w, ac[(size_t)s * D + t], num);
+  // Running state of this group: max, denominator and numerator relative to it.
+  float M = -INFINITY, den = 0.f, num[DPT];
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) num[x] = 0.f;
+  for (int s0 = g; s0 < nv; s0 += NG * NBAT) {
+    float2 mlv[NBAT];
+    float av[NBAT][DPT];
+    // All of the round's loads go out together.  The acc of an empty chunk was never
+    // written and may hold any bits: it is loaded but discarded by a select below.
+#pragma unroll
+    for (int i = 0; i < NBAT; ++i) {
+      const int s = s0 + i * NG;
+      mlv[i] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int x = 0; x < DPT; ++x) av[i][x] = 0.f;
+      if (s < nv) {
+        mlv[i] = *(const float2*)(ml + 2 * s);
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) av[i][x] = ac[(size_t)s * D + x * 64 + lane];
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < NBAT; ++i) Mb = fmaxf(Mb, mlv[i].x);
+    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
+    den *= sc;
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) num[x] *= sc;
+#pragma unroll
+    for (int i = 0; i < NBAT; ++i) {
+      const bool live = mlv[i].x != -INFINITY;
+      const float w = live ? fast_exp2(mlv[i].x - Mb) : 0.f;
+      den = live ? __builtin_fmaf(w, mlv[i].y, den) : den;
+#pragma unroll
+      for (int x = 0; x < DPT; ++x) num[x] = live ? __builtin_fmaf(w, av[i][x], num[x]) : num[x];
+    }
+    M = Mb;
   }
-  const float o = nv > 0 ? num / den : 0.f;
-  // Pair up neighbouring lanes so each even lane stores one dword.
-  const float o_next = __shfl_down(o, 1);
-  if ((t & 1) == 0) *(uint32_t*)(p.o + pair * D + t) = pack2<DT>(o, o_next);
+  if (lane == 0) sm_M[g] = M;
+  __syncthreads();
+  float Mall = sm_M[0];
+#pragma unroll
+  for (int i = 1; i < NG; ++i) Mall = fmaxf(Mall, sm_M[i]);
+  const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mall);
+  if (lane == 0) sm_den[g] = den * sc;
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) sm_num[g][x * 64 + lane] = num[x] * sc;
+  __syncthreads();
+  if (g == 0) {
+    float dn = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) dn += sm_den[i];
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) {
+      const int d = x * 64 + lane;
+      float nm = 0.f;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) nm += sm_num[i][d];
+      const float o = dn > 0.f ? nm / dn : 0.f;  // a length of 0 leaves every chunk empty
+      // Pair up neighbouring lanes so each even lane stores one dword.
+      const float o_next = __shfl_down(o, 1);
+      if ((lane & 1) == 0) *(uint32_t*)(p.o + pair * D + d) = pack2<DT>(o, o_next);
+    }
+  }
 }
 
 template <int DT, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<DT, D>), dim3(p.n_split, p.H, p.B), dim3(decode_cfg::kThreads), 0, st, p);
+  hipLaunchKernelGGL((decode_split_kernel<DT, D>), dim3(p.n_split, p.H, p.B), dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(D), 0, st, p);
+  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(decode_cfg::kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -39,9 +39,9 @@
 namespace attn {
 
 namespace prefill_cfg {
-constexpr int BN = 64;           // keys per tile
-constexpr float kLazyLog2 = 8.f;     // raise m only when a score exceeds it by > 2^8
-constexpr float kSumGuard = 4096.f;  // a unit's per-lane sum of p above this prompts a check
+[[maybe_unused]] constexpr int BN = 64;               // keys per tile
+[[maybe_unused]] constexpr float kLazyLog2 = 8.f;     // raise m only when a score exceeds it by > 2^8
+[[maybe_unused]] constexpr float kSumGuard = 4096.f;  // a unit's per-lane sum of p above this prompts a check
 }  // namespace prefill_cfg
 
 struct PrefillParams {

@@ -91,13 +91,13 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
 /* Rows of the decode split kernel's work granule: legal chunk sizes are multiples of it. */
 #define ATTN_DECODE_ROW_GRANULE 32
 
-/* Split workgroups per compute unit that the automatic decode split aims for. */
-#define ATTN_DECODE_WGS_PER_CU 2
+/* Split chunks (one wave each) per compute unit that the automatic decode split aims for. */
+#define ATTN_DECODE_WGS_PER_CU 8
 
 /* Host-only: the automatic decode split (page 3, "Kernel design": the chunk size is
- * chosen at launch so that even batch size 1 fills the GPU).  Aims at
- * ATTN_DECODE_WGS_PER_CU split workgroups per compute unit over the B*H (sequence,
- * head) pairs.  Writes the chunk (rows, a multiple of the granule) and the number of
+ * chosen at launch so that even batch size 1 fills the GPU).  Each chunk is one
+ * wave; aims at ATTN_DECODE_WGS_PER_CU chunks per compute unit over the B*H
+ * (sequence, head) pairs, without going below ATTN_DECODE_ROW_GRANULE rows.  Writes the chunk (rows, a multiple of the granule) and the number of
  * splits to the HOST pointers chunk and n_split.  No HIP call. */
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split);
 

@@ -7,7 +7,7 @@ import pytest
 
 import exact_attention_prefill_amd as ea
 
-WGS_PER_CU = 2
+WGS_PER_CU = 8
 G = ea.DECODE_ROW_GRANULE
 
 
@@ -26,13 +26,14 @@ def test_split_is_legal_and_covers(B, H, max_len, cus):
 
 
 def test_batch_one_fills_the_chip():
+    # 12 heads x 4096 rows: the smallest legal chunk gives 12 * 128 waves, six per CU.
     chunk, n = ea.decode_choose_split(1, 12, 4096, 64, 256)
-    assert (chunk, n) == (96, 43)
-    assert 12 * n >= 2 * 256
+    assert (chunk, n) == (32, 128)
+    assert 12 * n >= 256
 
 
 def test_batch_eight():
-    assert ea.decode_choose_split(8, 12, 4096, 64, 256) == (704, 6)
+    assert ea.decode_choose_split(8, 12, 4096, 64, 256) == (192, 22)
 
 
 def test_more_cus_never_larger_chunks():
