@@ -113,6 +113,14 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument(
+        "--calibrate-copy",
+        type=int,
+        default=0,
+        metavar="MIB",
+        help="after measuring, copy a MIB-sized buffer three times (a plain copy kernel of known "
+        "size that calibrates the HBM byte counters in a profiled run)",
+    )
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -213,6 +221,14 @@ def main():
     dref = oracle.decode(dq.double().numpy(), dk.double().numpy(), dv.double().numpy(), dl.numpy(), D.scale)
     derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
     log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}")
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
