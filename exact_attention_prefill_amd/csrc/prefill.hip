@@ -69,6 +69,32 @@ __device__ __forceinline__ u32x4 lds_read_b128(const uint16_t* lds_base, uint32_
   return *(const u32x4*)((const char*)lds_base + byte_off);
 }
 
+// One 16-byte-per-lane buffer load that writes LDS directly: lane i's 16 bytes from
+// rsrc + voff land at LDS byte address lds_addr + 16 i.  Issued from inline assembly
+// so the compiler does not track it: its own tracking cannot tell which LDS array a
+// transpose read touches and would drain every load in flight before each V read.
+// The kernel orders these loads itself: every buffer is read only after an
+// s_waitcnt vmcnt(0) and a barrier that follow the loads into it, and is reloaded
+// only after a barrier that follows every read of it.
+// m0 is a reserved register that nothing else in these kernels reads or writes; the
+// clobber records that the assembly overwrites it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %0, 0 offen lds"
+      :
+      : "s"(rsrc), "v"(voff), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // max(x, x of the lane 32 apart) and the sum likewise, from one v_permlane32_swap:
 // it returns (x with its upper half replaced by the partner's lower half, and the
 // partner half's view), so the two results hold {x, partner} in some order.
@@ -234,11 +260,13 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
     const int k0 = t * BN;
     const int rows_left = N - k0;
     const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RB;
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(src_base + (size_t)k0 * RB), 0, nrec, 0x00020000);
+    // Buffer descriptor: base address, stride 0, nrec bytes in range (rows past the
+    // end read nothing), raw dword format.
+    const uint64_t base = (uint64_t)(uintptr_t)(src_base + (size_t)k0 * RB);
+    const u32x4 r = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, nrec, 0x00020000u};
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst) + wave * NLD * 1024);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * NLD + i) * 1024), 16, offs[i], 0, 0, 0);
+    for (int i = 0; i < NLD; ++i) lds_dma16(r, offs[i], l0 + i * 1024);
   };
   auto load_k = [&](int t, char* dst) __attribute__((always_inline)) { load_tile(kbase, ldk_off, t, dst); };
   auto load_v = [&](int t, char* dst) __attribute__((always_inline)) { load_tile(vbase, ldv_off, t, dst); };
