@@ -19,7 +19,7 @@
 //
 // Staging: K and V tiles go from HBM/L2 straight into LDS with buffer loads that
 // write LDS (no registers, no VALU), 16 bytes per lane, in row-major order with the
-// 16-byte chunks of each row XOR-swizzled by (row mod 8) so the MFMA operand reads
+// 16-byte chunks of each row XOR-swizzled by a per-row key so the MFMA operand reads
 // are free of bank conflicts.  V^T operands are read with the LDS transpose load
 // (ds_read_b64_tr_b16), which gathers four keys of one d column per lane.  Rows past
 // the end of the sequence fall outside the buffer's range and are not loaded.
@@ -188,12 +188,15 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
     }
 
   // Tile layout in LDS: row-major rows of RB bytes whose 16-byte chunks are permuted
-  // by XOR with a per-row key, chosen (by measurement) so that both operand reads are
-  // free of bank conflicts: the K reads (16 consecutive rows, one chunk each) and the
-  // V^T transpose reads (8 rows x 4 chunks).  K: row & 15 (d=128) or (row>>1) & 7
-  // (d=64); V: 2*(row & 7) (d=128) or row & 7 (d=64).
+  // by XOR with a per-row key so that both operand reads are free of bank conflicts
+  // (64 banks of 4 bytes; a wave's read is served 256 bytes per cycle, in halves of 32
+  // lanes for the transpose reads).  K reads (one chunk of each of 32 consecutive
+  // rows; 16 rows per pass): key row & 15 (d=128) or (row>>1) & 7 (d=64).  V^T
+  // transpose reads (per 32-lane half: 4 rows x 4 consecutive chunks): the four rows
+  // must land on four disjoint 64-byte bank groups, key 4*(row & 3) (d=128, rows of
+  // 256 B) or 4*((row>>1) & 1) (d=64, rows of 128 B, odd rows already offset by 128 B).
   auto kkey = [](int row) __attribute__((always_inline)) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
-  auto vkey = [](int row) __attribute__((always_inline)) { return D == 128 ? ((row & 7) << 1) : (row & 7); };
+  auto vkey = [](int row) __attribute__((always_inline)) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
   // LDS-direct load r of this wave fills LDS chunk ci = (wave*NLD + r)*64 + lane, i.e.
   // row ci / (RB/16) and physical slot ci % (RB/16), which holds logical chunk
   // slot ^ key(row): fetch that chunk from memory.
