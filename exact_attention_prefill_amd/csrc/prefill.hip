@@ -9,8 +9,8 @@
 // (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation), the step page 3 lists as
 // missing from its own kernel ("Limitations", "Future work").
 //
-// Work decomposition: one workgroup of 4 waves per (128-query block, head, batch);
-// each wave owns 32 query rows.  Scores are computed transposed, S^T = K Q^T, so that
+// Work decomposition: one workgroup of 4 or 8 waves per (128- or 256-query block,
+// head, batch); each wave owns 32 query rows.  Scores are computed transposed, S^T = K Q^T, so that
 // in the MFMA result layout every lane holds 16 scores of ONE query row per 32-key
 // block: row max and row sum are in-lane reductions plus one exchange with the lane
 // 32 apart (v_permlane32_swap), and the output rescale is a per-lane scalar.  After
@@ -346,18 +346,26 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   // iteration's MFMAs, about three VALU instructions (one exponential) per MFMA, with
   // each dependent step in a later slot than its input.
   // scur = S_{u+1} (scored last iteration), snext receives S_{u+2}; pcur = P_u,
-  // pnext receives P_{u+1}.  kb_/h_k locate K of unit u+2, vb_/h_v V of unit u.
+  // pnext receives P_{u+1}.  kb_ holds K of unit u+2 and vb_ V of unit u, each in half h.
   // Near the end of a wave's range S_{u+2} may score keys it never uses: such a unit
   // is fully masked when it is consumed, so m and l do not move and P is zero.
   // Eight issue slots per iteration.  d = 128: slot i issues score MFMA i and P*V MFMA
   // i (s = i/4, db = i%4).  d = 64 (4 + 4 MFMAs): even slots score, odd slots P*V.
   // Each K or V operand read feeds the MFMAs of all QB row blocks.
+  // Operands are read PF MFMAs ahead into a ring of PF + 1 registers that spans the
+  // tile: operand a of the tile's unit h sits in slot (h*KS + a) mod (PF + 1) (K) or
+  // (h*NP + a) mod (PF + 1) (V), so the first unit of a tile already reads the second
+  // unit's leading operands (same buffers, no barrier between them) and only the
+  // first unit after a barrier starts with reads of its own.
   constexpr int NP = 2 * DB;  // P*V MFMAs per unit and row block
   constexpr int PF = 2;       // operand prefetch distance (MFMAs of the same kind)
+  constexpr int R = PF + 1;   // operand ring size
   auto s_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 0 ? i >> 1 : -1); };
   auto p_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 1 ? i >> 1 : -1); };
   auto iterate = [&](int u, f32x16 (&scur)[QB], f32x16 (&snext)[QB], const u32x4 (&pcur)[QB][2],
-                     u32x4 (&pnext)[QB][2], const char* kb_, int h_k, const char* vb_, int h_v) __attribute__((always_inline)) {
+                     u32x4 (&pnext)[QB][2], const char* kb_, const char* vb_, int h, u32x4 (&kf)[R],
+                     u32x4 (&vf)[R]) __attribute__((always_inline)) {
+    const int kg = h * KS, vg = h * NP;  // ring positions of this unit's operand 0
     float l_unit[QB];
     float xa[QB][2], xb[QB][2];  // P arguments / exponentials in flight, two dwords apart
 #pragma unroll
@@ -365,28 +373,24 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
       mask_unit(scur[cb], u + 1, cb);  // a unit past this wave's keys masks entirely: p = 0
       l_unit[cb] = 0.f;
     }
-    u32x4 kf[PF + 1], vf[PF + 1];
-#pragma unroll
-    for (int a = 0; a < PF; ++a) {
-      kf[a] = kread(kb_, h_k, a);
-      vf[a] = vread(vb_, h_v, a / DB, a % DB);
-    }
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) p_arg(scur[cb], neg_m[cb], 0, xa[cb]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int a = s_at(i), b = p_at(i);
       if (a >= 0) {
-        if (a + PF < KS) kf[(a + PF) % (PF + 1)] = kread(kb_, h_k, a + PF);
+        if (a + PF < KS) kf[(kg + a + PF) % R] = kread(kb_, h, a + PF);
+        else if (h == 0) kf[(kg + a + PF) % R] = kread(kb_, 1, a + PF - KS);
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb)  // the first MFMA of a chain takes a literal zero addend
-          snext[cb] = mfma32x32x16<DT>(kf[a % (PF + 1)], qf[cb][a], a == 0 ? (f32x16){} : snext[cb]);
+          snext[cb] = mfma32x32x16<DT>(kf[(kg + a) % R], qf[cb][a], a == 0 ? (f32x16){} : snext[cb]);
       }
       if (b >= 0) {
-        if (b + PF < NP) vf[(b + PF) % (PF + 1)] = vread(vb_, h_v, (b + PF) / DB, (b + PF) % DB);
+        if (b + PF < NP) vf[(vg + b + PF) % R] = vread(vb_, h, (b + PF) / DB, (b + PF) % DB);
+        else if (h == 0) vf[(vg + b + PF) % R] = vread(vb_, 1, (b + PF - NP) / DB, (b + PF - NP) % DB);
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb)
-          oacc[cb][b % DB] = mfma32x32x16<DT>(vf[b % (PF + 1)], pcur[cb][b / DB], oacc[cb][b % DB]);
+          oacc[cb][b % DB] = mfma32x32x16<DT>(vf[(vg + b) % R], pcur[cb][b / DB], oacc[cb][b % DB]);
       }
       // slot i: exponentials of dword i, pack of dword i-1, arguments of dword i+1
 #pragma unroll
@@ -468,8 +472,14 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
     if (t + 3 < nt) load_k(t + 3, kb_next);
   };
   auto tile = [&](int t, char* kb_next, char* vb_cur) __attribute__((always_inline)) {
-    if (2 * t < nu_w) iterate(2 * t, sy, sx, pa, pb, kb_next, 0, vb_cur, 0);
-    if (2 * t + 1 < nu_w) iterate(2 * t + 1, sx, sy, pb, pa, kb_next, 1, vb_cur, 1);
+    u32x4 kf[R], vf[R];
+#pragma unroll
+    for (int a = 0; a < PF; ++a) {
+      kf[a] = kread(kb_next, 0, a);
+      vf[a] = vread(vb_cur, 0, a / DB, a % DB);
+    }
+    if (2 * t < nu_w) iterate(2 * t, sy, sx, pa, pb, kb_next, vb_cur, 0, kf, vf);
+    if (2 * t + 1 < nu_w) iterate(2 * t + 1, sx, sy, pb, pa, kb_next, vb_cur, 1, kf, vf);
     sync_and_load(t, kb_next, vb_cur);
   };
   for (int t = 0; t < nt; t += 2) {
@@ -509,11 +519,15 @@ static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
 
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStream_t s) {
-  // Four waves of 32 query rows, two workgroups per CU (two waves per SIMD).  The
-  // 64-row form (QB = 2) halves LDS operand traffic per MFMA but, at one wave per
-  // SIMD with its score accumulators in AGPRs, measured slower on the d = 128 bf16
-  // 16K-token shape (0.98 vs 1.10 PFLOP/s), so it is not selected.
-  (void)num_cus;
+  // Waves of 32 query rows, two per SIMD.  Eight waves per workgroup (256 query rows,
+  // one workgroup per CU) stage each K/V tile once for twice the rows of the
+  // four-wave form (128 rows, two workgroups per CU), halving L2-to-LDS traffic per
+  // MFMA; it pays (+2-3% at d = 128, 16K tokens) when the grid still gives every CU
+  // at least four such workgroups, and small grids keep the finer four-wave blocks.
+  // The 64-row form (QB = 2) halves LDS operand reads per MFMA but, at one wave per
+  // SIMD, measured 5-8% slower, so it is not selected.
+  const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
+  if (blocks8 >= 4LL * num_cus) return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
   return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
 }
 

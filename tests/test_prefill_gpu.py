@@ -86,6 +86,22 @@ def test_gpt2_sweep_4096_sampled(case):
     sampled_parity(case, 2, heads, nrows=64)
 
 
+# Grids of at least four 256-row blocks per CU take the eight-wave workgroups; these
+# shapes reach them with a ragged last block (N not a multiple of 256).
+LARGE_RAGGED = [
+    W.PrefillCase("prefill_b1_h64_n4000_d128_bf16_full", 1, 64, 4000, 128, "bf16", False, 1 / np.sqrt(128)),
+    W.PrefillCase("prefill_b1_h64_n4000_d128_bf16_causal", 1, 64, 4000, 128, "bf16", True, 1 / np.sqrt(128)),
+    W.PrefillCase("prefill_b2_h32_n4001_d64_f16_causal", 2, 32, 4001, 64, "f16", True, 0.125),
+    W.PrefillCase("prefill_b2_h32_n4001_d64_f16_full", 2, 32, 4001, 64, "f16", False, 0.125),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_RAGGED, ids=lambda c: c.name)
+def test_large_grid_ragged_sampled(case):
+    heads = [(0, 0), (case.B - 1, case.H - 1), (0, case.H // 2)]
+    sampled_parity(case, 3, heads, nrows=48)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3, 1.0, 1e-3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scale_values(scale, causal):
