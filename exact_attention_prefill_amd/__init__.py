@@ -23,6 +23,8 @@ ATTN_F16, ATTN_BF16 = 0, 1
 ATTN_OK = 0
 ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGNMENT, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = -1, -2, -3, -4, -5
 DECODE_ROW_GRANULE = 32
+DECODE_WGS_PER_CU = 8
+DECODE_MIN_CHUNK = 64
 
 # Every symbol include/attn.h declares.
 EXPORTS = (

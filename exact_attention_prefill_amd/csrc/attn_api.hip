@@ -114,15 +114,20 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
   const long long T = ATTN_DECODE_ROW_GRANULE;
   const long long pairs = (long long)B * H;
   const long long target = (long long)ATTN_DECODE_WGS_PER_CU * num_cus;
-  const long long max_splits = (max_len + T - 1) / T;
+  // Smallest chunk: ATTN_DECODE_MIN_CHUNK rows, or the whole (granule-rounded) cache
+  // when it is shorter.
+  const long long rounded_len = (max_len + T - 1) / T * T;
+  const long long cmin = rounded_len < ATTN_DECODE_MIN_CHUNK ? rounded_len : ATTN_DECODE_MIN_CHUNK;
+  const long long max_splits = (max_len + cmin - 1) / cmin;
   long long ns = (target + pairs - 1) / pairs;
   if (ns < 1) ns = 1;
   if (ns > max_splits) ns = max_splits;
   long long c = (max_len + ns - 1) / ns;
   c = (c + T - 1) / T * T;
+  if (c < cmin) c = cmin;
   // Rounding the chunk up to the granule can drop the split count below the target;
   // shrink it one granule at a time until the target is met again.
-  while (c > T && pairs * ((max_len + c - 1) / c) < target) c -= T;
+  while (c - T >= cmin && pairs * ((max_len + c - 1) / c) < target) c -= T;
   *chunk = (int)c;
   *n_split = (int)((max_len + c - 1) / c);
   return ok();

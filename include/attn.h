@@ -94,10 +94,16 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
 /* Split chunks (one wave each) per compute unit that the automatic decode split aims for. */
 #define ATTN_DECODE_WGS_PER_CU 8
 
+/* Smallest chunk the automatic decode split picks (a multiple of the granule): below it
+ * a wave's fixed work (query load, cross-lane combine, partial store) outweighs the
+ * parallelism it adds.  Explicit chunks in attn_decode_ex may still be one granule. */
+#define ATTN_DECODE_MIN_CHUNK 64
+
 /* Host-only: the automatic decode split (page 3, "Kernel design": the chunk size is
  * chosen at launch so that even batch size 1 fills the GPU).  Each chunk is one
  * wave; aims at ATTN_DECODE_WGS_PER_CU chunks per compute unit over the B*H
- * (sequence, head) pairs, without going below ATTN_DECODE_ROW_GRANULE rows.  Writes the chunk (rows, a multiple of the granule) and the number of
+ * (sequence, head) pairs, without going below ATTN_DECODE_MIN_CHUNK rows (or the
+ * whole cache when it is shorter).  Writes the chunk (rows, a multiple of the granule) and the number of
  * splits to the HOST pointers chunk and n_split.  No HIP call. */
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split);
 

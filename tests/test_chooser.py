@@ -7,8 +7,13 @@ import pytest
 
 import exact_attention_prefill_amd as ea
 
-WGS_PER_CU = 8
+WGS_PER_CU = ea.DECODE_WGS_PER_CU
 G = ea.DECODE_ROW_GRANULE
+CMIN = ea.DECODE_MIN_CHUNK
+
+
+def min_chunk(max_len):
+    return min(CMIN, -(-max_len // G) * G)
 
 
 @pytest.mark.parametrize(
@@ -16,19 +21,20 @@ G = ea.DECODE_ROW_GRANULE
 )
 def test_split_is_legal_and_covers(B, H, max_len, cus):
     chunk, n = ea.decode_choose_split(B, H, max_len, 64, cus)
-    assert chunk % G == 0 and chunk >= G
+    assert chunk % G == 0 and chunk >= min_chunk(max_len)
     assert chunk <= -(-max_len // G) * G
     assert n == -(-max_len // chunk)
     assert (n - 1) * chunk < max_len <= n * chunk
-    # Enough splits to give every CU its share, unless the cache is too short to split further.
+    # Enough splits to give every CU its share, unless the chunk is already the smallest.
     if n * B * H < WGS_PER_CU * cus:
-        assert chunk == G
+        assert chunk == min_chunk(max_len)
 
 
 def test_batch_one_fills_the_chip():
-    # 12 heads x 4096 rows: the smallest legal chunk gives 12 * 128 waves, six per CU.
+    # 12 heads x 4096 rows: the smallest automatic chunk (64 rows) gives 12 * 64 waves,
+    # three per CU.
     chunk, n = ea.decode_choose_split(1, 12, 4096, 64, 256)
-    assert (chunk, n) == (32, 128)
+    assert (chunk, n) == (64, 64)
     assert 12 * n >= 256
 
 
@@ -50,3 +56,14 @@ def test_chooser_rejects(bad):
     a.update(bad)
     with pytest.raises(ValueError):
         ea.decode_choose_split(a["B"], a["H"], a["max_len"], a["d"], a["cus"])
+
+
+def test_binding_constants_match_header():
+    import os
+    import re
+
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "attn.h")).read()
+    defs = dict(re.findall(r"#define (ATTN_DECODE_\w+) (\d+)", hdr))
+    assert int(defs["ATTN_DECODE_ROW_GRANULE"]) == ea.DECODE_ROW_GRANULE
+    assert int(defs["ATTN_DECODE_WGS_PER_CU"]) == ea.DECODE_WGS_PER_CU
+    assert int(defs["ATTN_DECODE_MIN_CHUNK"]) == ea.DECODE_MIN_CHUNK

@@ -109,6 +109,23 @@ def test_scale_values(scale, causal):
     full_parity(1, 2, 150, 128, "bf16", causal, scale, seed=6)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_raise_the_running_max(causal, d, dtype):
+    """Key magnitudes that grow along the sequence push each row's maximum up again
+    and again, well past the 2^8 margin the optimistic softmax keeps, so the rescale
+    path runs many times per row."""
+    B, H, N = 1, 3, 700
+    q, k, v = W.prefill_inputs(B, H, N, d, dtype, 21)
+    growth = (1.0 + 6.0 * torch.arange(N, dtype=torch.float32) / N).view(1, 1, N, 1)
+    k = (k.float() * growth).to(k.dtype)
+    scale = 2.0 / np.sqrt(d)
+    out = run(q, k, v, causal, scale)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal, scale)
+    check(f64(out), ref, dtype, f"growing scores d{d} {dtype} causal={causal}")
+
+
 def test_zero_query_gives_mean():
     q, k, v = W.prefill_inputs(1, 2, 300, 128, "bf16", 3)
     q = torch.zeros_like(q)
