@@ -24,6 +24,13 @@ Conventions (readings of the pages, all explicit):
     (page 3, "What can it do": decoding token t equals prefill row t);
   * masked scores are -inf, i.e. exactly zero weight.
 
+Grouped heads (a reading of page 3, "Future work", where grouped-query attention
+is served by repeating each K/V head for its group of query heads): K and V may
+carry fewer heads than Q.  With Hq query heads and Hkv K/V heads, Hkv divides Hq,
+and query head h reads K/V head h // (Hq // Hkv), the head that repeating each K/V
+head Hq // Hkv times in order would place at position h.  Hkv = Hq is ordinary
+multi-head attention, Hkv = 1 shares one K/V head among all query heads.
+
 Every function follows the definition above; ``decode_split`` additionally
 follows the split-and-merge description on page 3 ("Kernel design": split-K
 decode with partial (m, l, acc) merged exactly by a second pass) and is used only
@@ -37,6 +44,12 @@ import numpy as np
 ROW_BLOCK = 1024  # rows per matrix product; row blocking does not change any row's value
 
 
+def kv_head(h: int, hq: int, hkv: int) -> int:
+    """K/V head read by query head h (see the module notes on grouped heads)."""
+    assert hkv >= 1 and hq % hkv == 0, "the K/V head count must divide the query head count"
+    return h // (hq // hkv)
+
+
 def _softmax_average(s: np.ndarray, v: np.ndarray) -> np.ndarray:
     """Rows of weights exp(s - max) / sum, applied to v.  s: (R, K) with -inf allowed."""
     m = np.max(s, axis=1, keepdims=True)
@@ -46,7 +59,7 @@ def _softmax_average(s: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float) -> np.ndarray:
-    """Exact attention for (B, H, N, d) float64 arrays; returns (B, H, N, d) float64.
+    """Exact attention for q (B, H, N, d) and k, v (B, Hkv, N, d); returns (B, H, N, d).
 
     Page 3, "What is Attention?" / "The Problem": each row scores every
     (previous, if causal) key; the weights sum to one and combine the values.
@@ -55,13 +68,15 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: fl
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
-    assert k.shape == (B, H, N, d) and v.shape == (B, H, N, d)
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d)
     out = np.empty((B, H, N, d), dtype=np.float64)
     for b in range(B):
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             for r0 in range(0, N, ROW_BLOCK):
                 rows = np.arange(r0, min(N, r0 + ROW_BLOCK))
-                out[b, h, rows] = _rows(q[b, h], k[b, h], v[b, h], rows, causal, scale)
+                out[b, h, rows] = _rows(q[b, h], k[b, g], v[b, g], rows, causal, scale)
     return out
 
 
@@ -79,14 +94,16 @@ def prefill_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows) -> n
     Used to check outputs at sizes where the full oracle would take minutes.
     """
     rows = np.asarray(rows, dtype=np.int64)
+    g = kv_head(h, q.shape[1], k.shape[1])
     qh = np.asarray(q[b, h], dtype=np.float64)
-    kh = np.asarray(k[b, h], dtype=np.float64)
-    vh = np.asarray(v[b, h], dtype=np.float64)
+    kh = np.asarray(k[b, g], dtype=np.float64)
+    vh = np.asarray(v[b, g], dtype=np.float64)
     return _rows(qh, kh, vh, rows, causal, scale)
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float) -> np.ndarray:
     """One query row per (b, h) over the first L_b cache rows; returns (B, H, 1, d).
+    The caches may carry Hkv heads (grouped heads).
 
     Page 3, "What can it do": one new token attends over a KV cache, with a
     different current length per sequence in the batch.
@@ -96,13 +113,15 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float) -> np.ndarray:
     vc = np.asarray(v_cache, dtype=np.float64)
     B, H, one, d = q.shape
     assert one == 1
+    Hkv = kc.shape[1]
     out = np.empty((B, H, 1, d), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
         assert 1 <= L <= kc.shape[2], "cache length must lie in [1, max_len]"
         for h in range(H):
-            s = float(scale) * (q[b, h] @ kc[b, h, :L].T)  # (1, L)
-            out[b, h] = _softmax_average(s, vc[b, h, :L])
+            g = kv_head(h, H, Hkv)
+            s = float(scale) * (q[b, h] @ kc[b, g, :L].T)  # (1, L)
+            out[b, h] = _softmax_average(s, vc[b, g, :L])
     return out
 
 
@@ -121,20 +140,22 @@ def decode_split(q, k_cache, v_cache, seq_lens, scale: float, chunk: int) -> np.
     kc = np.asarray(k_cache, dtype=np.float64)
     vc = np.asarray(v_cache, dtype=np.float64)
     B, H, _, d = q.shape
+    Hkv = kc.shape[1]
     out = np.empty((B, H, 1, d), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
         assert 1 <= L <= kc.shape[2]
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             ms, ls, accs = [], [], []
             for c0 in range(0, L, chunk):
                 c1 = min(L, c0 + chunk)
-                s = float(scale) * (kc[b, h, c0:c1] @ q[b, h, 0])  # (C,)
+                s = float(scale) * (kc[b, g, c0:c1] @ q[b, h, 0])  # (C,)
                 m = np.max(s)
                 p = np.exp(s - m)
                 ms.append(m)
                 ls.append(np.sum(p))
-                accs.append(p @ vc[b, h, c0:c1])
+                accs.append(p @ vc[b, g, c0:c1])
             M = max(ms)
             wts = [np.exp(m - M) for m in ms]
             num = sum(w * a for w, a in zip(wts, accs))

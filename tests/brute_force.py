@@ -18,12 +18,21 @@ def _attend(qrow, krows, vrows, scale):
     return [math.fsum(w[j] * vrows[j][c] for j in range(len(vrows))) / total for c in range(d)]
 
 
+def _expand(heads, hq):
+    """The K/V heads a query-head list of length hq reads: each of the Hkv heads
+    serves the next run of hq // Hkv query heads (grouped-query attention served by
+    repeating every K/V head for its group)."""
+    group = hq // len(heads)
+    assert group * len(heads) == hq
+    return [kvh for kvh in heads for _ in range(group)]
+
+
 def prefill(q, k, v, causal, scale):
-    """q, k, v nested lists [B][H][N][d] of floats; returns the same nesting."""
+    """q [B][H][N][d], k and v [B][Hkv][N][d] nested lists; returns [B][H][N][d]."""
     out = []
     for qb, kb, vb in zip(q, k, v):
         ob = []
-        for qh, kh, vh in zip(qb, kb, vb):
+        for qh, kh, vh in zip(qb, _expand(kb, len(qb)), _expand(vb, len(qb))):
             oh = []
             for i, qrow in enumerate(qh):
                 n = i + 1 if causal else len(kh)
@@ -34,9 +43,10 @@ def prefill(q, k, v, causal, scale):
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale):
-    """q [B][H][1][d], caches [B][H][max_len][d]; returns [B][H][1][d]."""
+    """q [B][H][1][d], caches [B][Hkv][max_len][d]; returns [B][H][1][d]."""
     out = []
     for b, (qb, kb, vb) in enumerate(zip(q, k_cache, v_cache)):
         L = int(seq_lens[b])
-        out.append([[_attend(qh[0], kh[:L], vh[:L], scale)] for qh, kh, vh in zip(qb, kb, vb)])
+        out.append([[_attend(qh[0], kh[:L], vh[:L], scale)]
+                    for qh, kh, vh in zip(qb, _expand(kb, len(qb)), _expand(vb, len(qb)))])
     return out

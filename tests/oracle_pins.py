@@ -258,6 +258,65 @@ def pin_library_sdpa(O):
         assert np.max(np.abs(got - ref)) <= 1e-12
 
 
+def pin_grouped_heads_brute_force(O):
+    """Grouped K/V heads: the oracle agrees with brute force, which builds each query
+    head's K/V by repeating every K/V head for its group."""
+    r = _rng(30)
+    for (B, Hq, Hkv, N, d) in [(1, 6, 2, 7, 3), (2, 4, 1, 5, 2), (1, 3, 3, 6, 4)]:
+        q = r.standard_normal((B, Hq, N, d))
+        k, v = r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hkv, N, d))
+        for causal in (False, True):
+            got = O.prefill(q, k, v, causal, 0.6)
+            ref = np.array(brute_force.prefill(_bf(q), _bf(k), _bf(v), causal, 0.6))
+            assert np.max(np.abs(got - ref)) <= 1e-13, (Hq, Hkv, causal)
+    q = r.standard_normal((2, 8, 1, 4))
+    kc, vc = r.standard_normal((2, 2, 9, 4)), r.standard_normal((2, 2, 9, 4))
+    for lens in ([9, 1], [4, 7]):
+        got = O.decode(q, kc, vc, lens, 0.8)
+        ref = np.array(brute_force.decode(_bf(q), _bf(kc), _bf(vc), lens, 0.8))
+        assert np.max(np.abs(got - ref)) <= 1e-13, lens
+
+
+def pin_grouped_heads_are_repeated_heads(O):
+    """Grouped K/V heads equal ordinary multi-head attention on K/V whose heads are
+    each repeated for their group, in prefill, row-sampled prefill, decode and split
+    decode."""
+    r = _rng(31)
+    B, Hq, Hkv, N, d = 2, 6, 3, 40, 8
+    g = Hq // Hkv
+    q = r.standard_normal((B, Hq, N, d))
+    k, v = r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hkv, N, d))
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    for causal in (False, True):
+        a = O.prefill(q, k, v, causal, 0.4)
+        assert np.max(np.abs(a - O.prefill(q, kr, vr, causal, 0.4))) <= 1e-14
+        rows = [0, 17, 39]
+        for h in (0, 3, 5):
+            part = O.prefill_rows(q, k, v, causal, 0.4, 1, h, rows)
+            assert np.max(np.abs(part - a[1, h, rows])) <= 1e-14
+    qd = r.standard_normal((B, Hq, 1, d))
+    lens = [40, 13]
+    base = O.decode(qd, k, v, lens, 0.4)
+    assert np.max(np.abs(base - O.decode(qd, kr, vr, lens, 0.4))) <= 1e-14
+    for C in (1, 7, 40):
+        assert np.max(np.abs(O.decode_split(qd, k, v, lens, 0.4, C) - base)) <= 1e-12, C
+
+
+def pin_grouped_heads_library_sdpa(O):
+    """Library special case for grouped heads: torch SDPA with enable_gqa, fp64 on the CPU."""
+    import torch
+
+    r = _rng(32)
+    q = r.standard_normal((2, 8, 33, 16))
+    k, v = r.standard_normal((2, 2, 33, 16)), r.standard_normal((2, 2, 33, 16))
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.3, enable_gqa=True
+        ).numpy()
+        got = O.prefill(q, k, v, causal, 0.3)
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
 PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -276,4 +335,7 @@ PINS = [
     pin_prefill_rows_matches_prefill,
     pin_split_invariance,
     pin_library_sdpa,
+    pin_grouped_heads_brute_force,
+    pin_grouped_heads_are_repeated_heads,
+    pin_grouped_heads_library_sdpa,
 ]

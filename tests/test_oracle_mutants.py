@@ -22,8 +22,11 @@ MUTATIONS = {
     "no_normalisation": ("return (w @ v) / l", "return (w @ v)"),
     "wrong_sum_axis": ("l = np.sum(w, axis=1, keepdims=True)", "l = np.sum(w, axis=0, keepdims=True)"),
     "reversed_values": ("return (w @ v) / l", "return (w @ v[::-1]) / l"),
-    "decode_excludes_current": ("(q[b, h] @ kc[b, h, :L].T)", "(q[b, h] @ kc[b, h, :L - 1].T)"),
-    "decode_values_offset": ("out[b, h] = _softmax_average(s, vc[b, h, :L])", "out[b, h] = _softmax_average(s, vc[b, h, 1:L + 1])"),
+    "decode_excludes_current": ("(q[b, h] @ kc[b, g, :L].T)", "(q[b, h] @ kc[b, g, :L - 1].T)"),
+    "decode_values_offset": ("out[b, h] = _softmax_average(s, vc[b, g, :L])", "out[b, h] = _softmax_average(s, vc[b, g, 1:L + 1])"),
+    "kv_head_modulo": ("return h // (hq // hkv)", "return h % hkv"),
+    "kv_head_last_of_group": ("return h // (hq // hkv)", "return min(hkv - 1, (h + 1) // (hq // hkv))"),
+    "prefill_values_head_zero": ("_rows(q[b, h], k[b, g], v[b, g], rows, causal, scale)", "_rows(q[b, h], k[b, g], v[b, 0], rows, causal, scale)"),
     "split_no_rescale": ("wts = [np.exp(m - M) for m in ms]", "wts = [1.0 for m in ms]"),
     "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
     "split_sign": ("wts = [np.exp(m - M) for m in ms]", "wts = [np.exp(M - m) for m in ms]"),
