@@ -35,6 +35,9 @@ EXPORTS = (
     "attn_decode_workspace_bytes",
     "attn_status_string",
     "attn_last_error",
+    "attn_prefill_gqa",
+    "attn_decode_gqa",
+    "attn_decode_gqa_choose_split",
 )
 
 _lib = None
@@ -75,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.attn_status_string.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_prefill_gqa.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.attn_prefill_gqa.restype = i
+        L.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_decode_gqa.restype = i
+        L.attn_decode_gqa_choose_split.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.attn_decode_gqa_choose_split.restype = i
         _lib = L
     return _lib
 
@@ -114,18 +123,28 @@ def _stream(device) -> int:
 
 
 def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None):
-    """Exact attention for (B, H, N, d) fp16/bf16 GPU tensors; returns out (same shape/dtype)."""
-    if q.dim() != 4:
-        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q must be (batch, heads, seq_len, d)")
+    """Exact attention for fp16/bf16 GPU tensors q (B, H, N, d) and k, v (B, Hkv, N, d);
+    returns out shaped like q.  Hkv < H selects grouped K/V heads (query head h reads
+    K/V head h // (H // Hkv)); Hkv must divide H."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q, k, v must be (batch, heads, seq_len, d)")
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     if out is None:
         out = torch.empty_like(q)
-    ptrs = [_dev_tensor(t, n, q.dtype, (B, H, N, d)) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    pq = _dev_tensor(q, "q", q.dtype, (B, H, N, d))
+    pk = _dev_tensor(k, "k", q.dtype, (B, Hkv, N, d))
+    pv = _dev_tensor(v, "v", q.dtype, (B, Hkv, N, d))
+    po = _dev_tensor(out, "out", q.dtype, (B, H, N, d))
     with torch.cuda.device(q.device):
-        _check(lib().attn_prefill(*ptrs, B, H, N, d, dt, int(bool(causal)), float(scale), _stream(q.device)))
+        st = _stream(q.device)
+        if Hkv == H:
+            _check(lib().attn_prefill(pq, pk, pv, po, B, H, N, d, dt, int(bool(causal)), float(scale), st))
+        else:
+            _check(lib().attn_prefill_gqa(pq, pk, pv, po, B, H, Hkv, N, d, dt, int(bool(causal)), float(scale), st))
     return out
 
 
@@ -133,7 +152,8 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, 
            validate: bool = False):
     """One query row per (b, h) over the first seq_lens[b] cache rows.
 
-    q (B, H, 1, d); caches (B, H, max_len, d); seq_lens int32 GPU tensor (B,).
+    q (B, H, 1, d); caches (B, Hkv, max_len, d) with Hkv dividing H (grouped K/V heads
+    when Hkv < H); seq_lens int32 GPU tensor (B,).
     ``chunk``/``workspace`` select attn_decode_ex (0 = automatic chunk; workspace a
     GPU tensor of at least decode_workspace_bytes bytes).  ``validate`` checks on the
     host that every length lies in [1, max_len] (a device-to-host copy).
@@ -143,15 +163,15 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, 
     B, H, _, d = q.shape
     if k_cache.dim() != 4:
         raise AttnValueError(ATTN_ERR_INVALID_ARG, "k_cache must be (batch, heads, max_len, d)")
-    max_len = k_cache.shape[2]
+    Hkv, max_len = k_cache.shape[1], k_cache.shape[2]
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     if out is None:
         out = torch.empty_like(q)
     pq = _dev_tensor(q, "q", q.dtype, (B, H, 1, d))
-    pk = _dev_tensor(k_cache, "k_cache", q.dtype, (B, H, max_len, d))
-    pv = _dev_tensor(v_cache, "v_cache", q.dtype, (B, H, max_len, d))
+    pk = _dev_tensor(k_cache, "k_cache", q.dtype, (B, Hkv, max_len, d))
+    pv = _dev_tensor(v_cache, "v_cache", q.dtype, (B, Hkv, max_len, d))
     pl = _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
     po = _dev_tensor(out, "out", q.dtype, (B, H, 1, d))
     if validate:
@@ -160,12 +180,15 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, 
             raise AttnValueError(ATTN_ERR_INVALID_ARG, f"seq_lens must lie in [1, {max_len}]")
     with torch.cuda.device(q.device):
         st = _stream(q.device)
-        if chunk == 0 and workspace is None:
+        wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        if workspace is not None and workspace.device.type != "cuda":
+            raise AttnValueError(ATTN_ERR_INVALID_ARG, "workspace must be a GPU tensor")
+        if Hkv != H:
+            _check(lib().attn_decode_gqa(pq, pk, pv, pl, po, B, H, Hkv, max_len, d, dt, float(scale), int(chunk),
+                                         wp or None, wb, st))
+        elif chunk == 0 and workspace is None:
             _check(lib().attn_decode(pq, pk, pv, pl, po, B, H, max_len, d, dt, float(scale), st))
         else:
-            wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
-            if workspace is not None and workspace.device.type != "cuda":
-                raise AttnValueError(ATTN_ERR_INVALID_ARG, "workspace must be a GPU tensor")
             _check(lib().attn_decode_ex(pq, pk, pv, pl, po, B, H, max_len, d, dt, float(scale), int(chunk),
                                         wp or None, wb, st))
     return out
@@ -175,6 +198,13 @@ def decode_choose_split(B: int, H: int, max_len: int, d: int, num_cus: int):
     """(chunk, n_split) the automatic decode split picks for a device with num_cus CUs."""
     c, n = ctypes.c_int(0), ctypes.c_int(0)
     _check(lib().attn_decode_choose_split(B, H, max_len, d, num_cus, ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value
+
+
+def decode_gqa_choose_split(B: int, Hq: int, Hkv: int, max_len: int, d: int, num_cus: int):
+    """(chunk, n_split) the automatic decode split picks with grouped K/V heads."""
+    c, n = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().attn_decode_gqa_choose_split(B, Hq, Hkv, max_len, d, num_cus, ctypes.byref(c), ctypes.byref(n)))
     return c.value, n.value
 
 

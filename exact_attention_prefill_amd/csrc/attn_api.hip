@@ -12,10 +12,12 @@
 #include "attn.h"
 
 namespace attn {
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int dt,
-                          int causal, float scale, int num_cus, hipStream_t s);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
+                          int dt, int causal, float scale, int num_cus, hipStream_t s);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
-                         int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws, hipStream_t st);
+                         int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
+                         hipStream_t st);
+int decode_heads_per_wave(int H, int Hkv);
 }  // namespace attn
 
 namespace {
@@ -46,6 +48,12 @@ int check_common(int B, int H, int rows, int d, int dtype, float scale, const ch
   // Element offsets are formed in 64 bits, but per-head row counts and grid sizes stay in int.
   const long long elems = (long long)B * H * rows;
   if (elems > (1LL << 40) / d) return fail(ATTN_ERR_INVALID_ARG, "tensor too large");
+  return ATTN_OK;
+}
+
+int check_heads(int H, int Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must divide the query head count H=%d", Hkv, H);
   return ATTN_OK;
 }
 
@@ -91,19 +99,30 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int dtype,
-                 int causal, float scale, void* stream) {
+static int prefill_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int N, int d,
+                        int dtype, int causal, float scale, void* stream) {
   int st;
   if ((st = check_common(B, H, N, d, dtype, scale, "N")) != ATTN_OK) return st;
+  if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
     return st;
   if (out == q || out == k || out == v) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
   int cus = 0;
   if ((st = device_cus(&cus)) != ATTN_OK) return st;
-  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, N, d, dtype, causal, scale, cus, (hipStream_t)stream);
+  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, Hkv, N, d, dtype, causal, scale, cus, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int dtype,
+                 int causal, float scale, void* stream) {
+  return prefill_impl(q, k, v, out, B, H, H, N, d, dtype, causal, scale, stream);
+}
+
+int attn_prefill_gqa(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
+                     int dtype, int causal, float scale, void* stream) {
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
 }
 
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {
@@ -133,16 +152,24 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
   return ok();
 }
 
+int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split) {
+  if (Hq < 1 || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must divide the query head count Hq=%d", Hkv, Hq);
+  // One wave serves decode_heads_per_wave query heads: that many fewer waves per split.
+  return attn_decode_choose_split(B, Hq / attn::decode_heads_per_wave(Hq, Hkv), max_len, d, num_cus, chunk, n_split);
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d) {
   if (B < 1 || H < 1 || n_split < 1 || d < 1) return 0;
   return (size_t)B * H * n_split * (size_t)(d + 2) * sizeof(float);
 }
 
 static int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
-                       int B, int H, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
+                       int B, int H, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
                        size_t ws_bytes, void* stream, bool caller_ws) {
   int st;
   if ((st = check_common(B, H, max_len, d, dtype, scale, "max_len")) != ATTN_OK) return st;
+  if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
       (st = check_ptr(out, "out")))
     return st;
@@ -160,7 +187,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   if (chunk == 0) {
     int cus = 0;
     if ((st = device_cus(&cus)) != ATTN_OK) return st;
-    if ((st = attn_decode_choose_split(B, H, max_len, d, cus, &chunk, &n_split)) != ATTN_OK) return st;
+    if ((st = attn_decode_gqa_choose_split(B, H, Hkv, max_len, d, cus, &chunk, &n_split)) != ATTN_OK) return st;
   } else {
     n_split = (max_len + chunk - 1) / chunk;
   }
@@ -175,7 +202,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   } else if (ws_bytes < need) {
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
   }
-  hipError_t e = attn::launch_decode(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, chunk,
+  hipError_t e = attn::launch_decode(q, k_cache, v_cache, seq_lens, out, B, H, Hkv, max_len, d, dtype, scale, chunk,
                                      n_split, (float*)ws, s);
   if (own) {
     hipError_t e2 = hipFreeAsync(ws, s);
@@ -187,14 +214,21 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, int B,
                 int H, int max_len, int d, int dtype, float scale, void* stream) {
-  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, 0, nullptr, 0, stream, false);
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, H, max_len, d, dtype, scale, 0, nullptr, 0, stream, false);
 }
 
 int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, int B,
                    int H, int max_len, int d, int dtype, float scale, int chunk, void* workspace, size_t ws_bytes,
                    void* stream) {
-  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, max_len, d, dtype, scale, chunk, workspace, ws_bytes,
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, H, H, max_len, d, dtype, scale, chunk, workspace, ws_bytes,
                      stream, true);
+}
+
+int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, int B,
+                    int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, max_len, d, dtype, scale, chunk, workspace,
+                     ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -38,10 +38,23 @@ struct DecodeParams {
   float* ws_acc;
   float* ws_ml;
   int B, H, max_len, chunk, n_split;
-  float c;  // scale * log2(e), any sign
+  int Hkv, g;  // K/V heads and query heads per K/V head (H = Hkv * g)
+  float c;     // scale * log2(e), any sign
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
+
+// Dot product of two packed pairs of 16-bit values, accumulated in fp32.
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc);
+template <>
+__device__ __forceinline__ float dot2<DT_BF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+template <>
+__device__ __forceinline__ float dot2<DT_F16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
 
 // Combine two online-softmax states (m, l, acc[8]) exactly: the larger m wins and the
 // other side is scaled by 2^(m_other - m).  m = -inf means empty.
@@ -55,43 +68,51 @@ __device__ __forceinline__ void combine(float& m, float& l, float (&acc)[8], flo
   for (int x = 0; x < 8; ++x) acc[x] = acc[x] * a + acc2[x] * b;
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_split_kernel(DecodeParams p) {
+// One wave per (split, group of G query heads, batch).  The G heads share one K/V
+// head (grouped heads: G divides the group size g), so the wave streams that head's
+// cache rows once and keeps G online-softmax states; for each head the arithmetic
+// is exactly that of a single-head wave.  Scores: q . k from packed 16-bit pairs
+// (v_dot2, fp32 accumulation), summed over the row's lanes, then times scale*log2(e).
+// V rows are widened to fp32 once and shared by the G heads.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_split_kernel(
+    DecodeParams p) {
   using namespace decode_cfg;
   constexpr int LPR = D / 8;      // lanes per cache row
   constexpr int RPW = 64 / LPR;   // rows per wave-wide load
   constexpr int RITER = RPW * kUnroll;
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int h0 = blockIdx.y * G;  // first query head of this wave
+  const int kvh = h0 / p.g;       // the K/V head all G of them read
   const int L = clamp_len(p.seq_lens[b], p.max_len);
   const int r0 = s * p.chunk;
   const int lane = threadIdx.x;
-  const size_t pair = (size_t)b * p.H + h;
-  const size_t pidx = pair * p.n_split + s;
+  const size_t pair0 = (size_t)b * p.H + h0;  // (b, h0) as a query-head pair index
   if (r0 >= L) {  // empty chunk: mark it so the merge needs no lengths
-    if (lane == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(-INFINITY, 0.f);
+    if (lane < G) *(float2*)(p.ws_ml + ((pair0 + lane) * p.n_split + s) * 2) = make_float2(-INFINITY, 0.f);
     return;
   }
   const int r1 = min(L, r0 + p.chunk);
 
   const int seg = lane % LPR;   // which 8 elements of d
   const int rsub = lane / LPR;  // row within one wave-wide load
-  const uint16_t* kg = p.k + pair * p.max_len * D + seg * 8;
-  const uint16_t* vg = p.v + pair * p.max_len * D + seg * 8;
+  const size_t kvpair = (size_t)b * p.Hkv + kvh;
+  const uint16_t* kg = p.k + kvpair * p.max_len * D + seg * 8;
+  const uint16_t* vg = p.v + kvpair * p.max_len * D + seg * 8;
 
-  float qv[8];
-  {
-    const u32x4 t = *(const u32x4*)(p.q + pair * D + seg * 8);
+  u32x4 qp[G];  // this lane's 8 elements of each head's query row, packed as stored
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      qv[2 * x] = to_f32<DT>(t[x] & 0xffffu) * p.c;
-      qv[2 * x + 1] = to_f32<DT>(t[x] >> 16) * p.c;
-    }
+  for (int j = 0; j < G; ++j) qp[j] = *(const u32x4*)(p.q + (pair0 + j) * D + seg * 8);
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[j][x] = 0.f;
   }
-
-  float m = -INFINITY, l = 0.f, acc[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) acc[x] = 0.f;
 
   // Rows of one iteration: base + u*RPW + rsub.  The loads of iteration i+1 are
   // issued before iteration i is reduced, so a wave keeps two iterations in flight.
@@ -108,36 +129,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     }
   };
   auto reduce = [&](int base, const u32x4 (&kr)[kUnroll], const u32x4 (&vr)[kUnroll]) __attribute__((always_inline)) {
-    float sc[kUnroll];
-    float mx = m;
+    // V elements widened to fp32: once for all G heads, or at their single use (G = 1).
+    auto vx = [&](int u, int x) __attribute__((always_inline)) {
+      return to_f32<DT>((x & 1) ? (vr[u][x >> 1] >> 16) : (vr[u][x >> 1] & 0xffffu));
+    };
+    float vf[kUnroll][8];
+    if constexpr (G > 1) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float part = 0.f;
+      for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        part = __builtin_fmaf(qv[2 * x], to_f32<DT>(kr[u][x] & 0xffffu), part);
-        part = __builtin_fmaf(qv[2 * x + 1], to_f32<DT>(kr[u][x] >> 16), part);
-      }
-      // Sum the LPR lanes of this row (aligned groups of LPR consecutive lanes).
-#pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off);
-      sc[u] = base + u * RPW + rsub < r1 ? part : -INFINITY;
-      mx = fmaxf(mx, sc[u]);
+        for (int x = 0; x < 8; ++x) vf[u][x] = vx(u, x);
     }
-    if (mx != -INFINITY) {  // this row group has valid rows in this iteration
-      const float alpha = fast_exp2(m - mx);  // m = -inf gives 0
-      m = mx;
-      l *= alpha;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+    for (int j = 0; j < G; ++j) {
+      float sc[kUnroll];
+      float mx = m[j];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const float pu = fast_exp2(sc[u] - m);  // -inf gives 0
-        l += pu;
+        float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          acc[2 * x] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] & 0xffffu), acc[2 * x]);
-          acc[2 * x + 1] = __builtin_fmaf(pu, to_f32<DT>(vr[u][x] >> 16), acc[2 * x + 1]);
+        for (int x = 0; x < 4; ++x) part = dot2<DT>(qp[j][x], kr[u][x], part);
+        // Sum the LPR lanes of this row (aligned groups of LPR consecutive lanes).
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off);
+        sc[u] = base + u * RPW + rsub < r1 ? part * p.c : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      if (mx != -INFINITY) {  // this row group has valid rows in this iteration
+        const float alpha = fast_exp2(m[j] - mx);  // m = -inf gives 0
+        m[j] = mx;
+        l[j] *= alpha;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[j][x] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float pu = fast_exp2(sc[u] - m[j]);  // -inf gives 0
+          l[j] += pu;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[j][x] = __builtin_fmaf(pu, G > 1 ? vf[u][x] : vx(u, x), acc[j][x]);
         }
       }
     }
@@ -152,20 +181,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     reduce(base + RITER, kb, vb);
   }
 
-  // Combine the RPW row groups of the wave (lanes rsub*LPR + seg) pairwise.
+  // Combine the RPW row groups of the wave (lanes rsub*LPR + seg) pairwise, per head.
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    float acc2[8];
+  for (int j = 0; j < G; ++j) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc2[x] = __shfl_xor(acc[x], off);
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-    combine(m, l, acc, m2, l2, acc2);
+    for (int off = LPR; off < 64; off <<= 1) {
+      float acc2[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc2[x] = __shfl_xor(acc[j][x], off);
+      const float m2 = __shfl_xor(m[j], off), l2 = __shfl_xor(l[j], off);
+      combine(m[j], l[j], acc[j], m2, l2, acc2);
+    }
   }
   if (rsub == 0) {
-    float* out = p.ws_acc + pidx * D + seg * 8;
-    *(f32x4*)out = (f32x4){acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4*)(out + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]};
-    if (seg == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(m, l);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const size_t pidx = (pair0 + j) * p.n_split + s;
+      float* out = p.ws_acc + pidx * D + seg * 8;
+      *(f32x4*)out = (f32x4){acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      *(f32x4*)(out + 4) = (f32x4){acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
+      if (seg == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(m[j], l[j]);
+    }
   }
 }
 
@@ -255,17 +291,40 @@ __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int G>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<DT, D>), dim3(p.n_split, p.H, p.B), dim3(64), 0, st, p);
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(p.n_split, p.H / G, p.B), dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(decode_cfg::kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 
+template <int DT, int D>
+static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_decode_t<DT, D, 1>(p, st);
+    case 2: return launch_decode_t<DT, D, 2>(p, st);
+    case 3: return launch_decode_t<DT, D, 3>(p, st);
+    case 4: return launch_decode_t<DT, D, 4>(p, st);
+    case 5: return launch_decode_t<DT, D, 5>(p, st);
+    case 6: return launch_decode_t<DT, D, 6>(p, st);
+    case 7: return launch_decode_t<DT, D, 7>(p, st);
+    case 8: return launch_decode_t<DT, D, 8>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int decode_heads_per_wave(int H, int Hkv) {
+  const int g = H / Hkv;
+  for (int G = 8; G > 1; --G)
+    if (g % G == 0) return G;
+  return 1;
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
-                         int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws, hipStream_t st) {
+                         int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
+                         hipStream_t st) {
   DecodeParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -276,14 +335,17 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
   p.ws_ml = ws + (size_t)B * H * n_split * d;
   p.B = B;
   p.H = H;
+  p.Hkv = Hkv;
+  p.g = H / Hkv;
   p.max_len = max_len;
   p.chunk = chunk;
   p.n_split = n_split;
   p.c = scale * kLog2e;
-  if (dt == DT_F16 && d == 64) return launch_decode_t<DT_F16, 64>(p, st);
-  if (dt == DT_F16 && d == 128) return launch_decode_t<DT_F16, 128>(p, st);
-  if (dt == DT_BF16 && d == 64) return launch_decode_t<DT_BF16, 64>(p, st);
-  if (dt == DT_BF16 && d == 128) return launch_decode_t<DT_BF16, 128>(p, st);
+  const int G = decode_heads_per_wave(H, Hkv);
+  if (dt == DT_F16 && d == 64) return launch_decode_g<DT_F16, 64>(p, G, st);
+  if (dt == DT_F16 && d == 128) return launch_decode_g<DT_F16, 128>(p, G, st);
+  if (dt == DT_BF16 && d == 64) return launch_decode_g<DT_BF16, 64>(p, G, st);
+  if (dt == DT_BF16 && d == 128) return launch_decode_g<DT_BF16, 128>(p, G, st);
   return hipErrorInvalidValue;
 }
 

@@ -50,6 +50,7 @@ struct PrefillParams {
   const uint16_t* v;
   uint16_t* o;
   int B, H, N;
+  int g;          // query heads per K/V head (grouped heads; 1 for multi-head)
   int nqblk;      // ceil(N / BM), BM = 32 * waves per workgroup
   float c;        // |scale| * log2(e) (> 0); log2(e) when scale == 0
   uint32_t qxor;  // 0x80008000 flips Q's sign (scale < 0), else 0
@@ -172,9 +173,13 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   for (int cb = 0; cb < QB; ++cb) qrow[cb] = qw0 + 32 * cb + l32;
 
   const size_t head_off = (size_t)bh * N * D;
+  // Query head h of batch b reads K/V head h / g; with H = Hkv * g that pair index is
+  // (b*H + h) / g = b*Hkv + h/g.
+  const int kvbh = __builtin_amdgcn_readfirstlane(bh / p.g);
+  const size_t kv_off = (size_t)kvbh * N * D;
   const uint16_t* __restrict__ qg = p.q + head_off;
-  const char* kbase = (const char*)(p.k + head_off);
-  const char* vbase = (const char*)(p.v + head_off);
+  const char* kbase = (const char*)(p.k + kv_off);
+  const char* vbase = (const char*)(p.v + kv_off);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8*half + 0..7].
   u32x4 qf[QB][KS];
@@ -531,8 +536,8 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
 }
 
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int dt,
-                          int causal, float scale, int num_cus, hipStream_t s) {
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
+                          int dt, int causal, float scale, int num_cus, hipStream_t s) {
   PrefillParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -541,6 +546,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   p.B = B;
   p.H = H;
   p.N = N;
+  p.g = H / Hkv;
   p.nqblk = 0;
   // Scores use c = |scale| log2(e) > 0 so the running max is a max of c*s; a negative
   // scale is carried by flipping Q's sign bits, a zero scale by a zero Q (all scores 0).

@@ -107,6 +107,35 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
  * splits to the HOST pointers chunk and n_split.  No HIP call. */
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split);
 
+/* Grouped K/V heads (grouped-query and multi-query attention; page 3, "Future work",
+ * where the pages serve it by repeating K/V heads on the host).  Q and the output
+ * keep Hq heads; K and V (or the caches) carry Hkv heads, Hkv dividing Hq, and query
+ * head h reads K/V head h / (Hq / Hkv): each K/V head serves a consecutive group of
+ * query heads, as repeating it in place would.  Hkv == Hq is ordinary multi-head
+ * attention and gives the same results as attn_prefill / attn_decode_ex; Hkv == 1
+ * is multi-query attention.  Everything else (layout, dtype, validation, ownership,
+ * asynchrony) is as for the multi-head entry points; a Hkv that does not divide Hq
+ * returns ATTN_ERR_INVALID_ARG.
+ *
+ * attn_prefill_gqa: q, out [B][Hq][N][d]; k, v [B][Hkv][N][d].  Allocates nothing. */
+int attn_prefill_gqa(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
+                     int dtype, int causal, float scale, void* stream);
+
+/* attn_decode_gqa: q, out [B][Hq][1][d]; k_cache, v_cache [B][Hkv][max_len][d].
+ * chunk / workspace / ws_bytes as for attn_decode_ex (chunk 0: automatic, from
+ * attn_decode_gqa_choose_split; workspace NULL with ws_bytes 0: stream-ordered
+ * allocation).  The workspace holds partials per query head:
+ * attn_decode_workspace_bytes(B, Hq, n_split, d).  Each split wave reads its K/V rows
+ * once for up to 8 query heads of one group, so the cache is read once per group of
+ * up to 8 heads rather than once per query head. */
+int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                    int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/* Host-only: the automatic split of attn_decode_gqa (writes HOST *chunk, *n_split).
+ * With Hkv == Hq it equals attn_decode_choose_split.  No HIP call. */
+int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split);
+
 /* Host-only: bytes of decode workspace for B*H*n_split partials of (m, l, acc[d]) fp32. */
 size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d);
 

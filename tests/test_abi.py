@@ -129,3 +129,65 @@ def test_last_error_is_thread_local():
 def test_workspace_bytes():
     assert ea.decode_workspace_bytes(8, 12, 6, 64) == 8 * 12 * 6 * 66 * 4
     assert ea.decode_workspace_bytes(0, 12, 6, 64) == 0
+
+
+def _prefill_gqa(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], B=1, Hq=8, Hkv=2, N=128, d=64, dt=0, causal=0, scale=0.125, s=None)
+    a.update(kw)
+    return ea.lib().attn_prefill_gqa(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                                     a["dt"], a["causal"], a["scale"], a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(Hkv=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG),  # does not divide 8
+        (dict(Hkv=16), ea.ATTN_ERR_INVALID_ARG),  # more K/V heads than query heads
+        (dict(Hq=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(d=80), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(k=P[1] + 4), ea.ATTN_ERR_ALIGNMENT),
+        (dict(out=P[1]), ea.ATTN_ERR_INVALID_ARG),
+    ],
+)
+def test_prefill_gqa_validation(kw, status):
+    assert _prefill_gqa(**kw) == status
+    assert ea.last_error() != ""
+
+
+def _decode_gqa(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], lens=P[4], out=P[3], B=2, Hq=6, Hkv=2, max_len=100, d=128, dt=1, scale=0.1,
+             chunk=32, ws=P[5], ws_bytes=1 << 20, s=None)
+    a.update(kw)
+    return ea.lib().attn_decode_gqa(a["q"], a["k"], a["v"], a["lens"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                    a["max_len"], a["d"], a["dt"], a["scale"], a["chunk"], a["ws"], a["ws_bytes"],
+                                    a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(Hkv=4), ea.ATTN_ERR_INVALID_ARG),
+        (dict(Hkv=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(Hkv=12), ea.ATTN_ERR_INVALID_ARG),
+        (dict(chunk=48), ea.ATTN_ERR_INVALID_ARG),
+        (dict(lens=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(ws_bytes=ea.decode_workspace_bytes(2, 6, 4, 128) - 1), ea.ATTN_ERR_WORKSPACE),
+        (dict(ws_bytes=ea.decode_workspace_bytes(2, 2, 4, 128)), ea.ATTN_ERR_WORKSPACE),  # sized per K/V head: too small
+    ],
+)
+def test_decode_gqa_validation(kw, status):
+    assert _decode_gqa(**kw) == status
+    assert ea.last_error() != ""
+
+
+def test_gqa_chooser():
+    # Equal head counts choose exactly as multi-head decode does.
+    for B, H in ((1, 12), (8, 12), (4, 32)):
+        assert ea.decode_gqa_choose_split(B, H, H, 4096, 64, 256) == ea.decode_choose_split(B, H, 4096, 64, 256)
+    # One wave serves up to 8 query heads of a group (the largest divisor of the group
+    # size that is at most 8): fewer waves per split, as for that many fewer heads.
+    for Hq, Hkv, waves in ((32, 8, 8), (12, 4, 4), (18, 1, 3), (14, 1, 2), (22, 2, 22), (64, 8, 8)):
+        assert ea.decode_gqa_choose_split(8, Hq, Hkv, 4096, 128, 256) == ea.decode_choose_split(8, waves, 4096, 128, 256)
+    with pytest.raises(ValueError):
+        ea.decode_gqa_choose_split(1, 8, 3, 100, 64, 256)

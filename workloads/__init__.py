@@ -88,6 +88,33 @@ def decode_inputs(B, H, max_len, d, dtype="f16", seed=0, seq_lens=None):
     return q, kc, vc, lens.to(torch.int32)
 
 
+def prefill_inputs_gqa(B, Hq, Hkv, N, d, dtype="f16", seed=0):
+    """Grouped heads: q (B, Hq, N, d), k and v (B, Hkv, N, d), drawn q, k, v in order."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    tdt = DTYPES[dtype]
+    q = torch.randn(B, Hq, N, d, generator=g, dtype=torch.float32).to(tdt)
+    k = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32).to(tdt)
+    v = torch.randn(B, Hkv, N, d, generator=g, dtype=torch.float32).to(tdt)
+    return q, k, v
+
+
+def decode_inputs_gqa(B, Hq, Hkv, max_len, d, dtype="f16", seed=0, seq_lens=None):
+    """Grouped heads: q (B, Hq, 1, d), caches (B, Hkv, max_len, d), lengths as in decode_inputs."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    tdt = DTYPES[dtype]
+    q = torch.randn(B, Hq, 1, d, generator=g, dtype=torch.float32).to(tdt)
+    kc = torch.randn(B, Hkv, max_len, d, generator=g, dtype=torch.float32).to(tdt)
+    vc = torch.randn(B, Hkv, max_len, d, generator=g, dtype=torch.float32).to(tdt)
+    if seq_lens is None:
+        if B == 1:
+            lens = torch.full((1,), max_len, dtype=torch.int64)
+        else:
+            lens = torch.randint(1, max_len + 1, (B,), generator=g)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    return q, kc, vc, lens.to(torch.int32)
+
+
 def prefill_rows_sample(N, count, seed=0, include_edges=True):
     """Row indices for sampled parity at full size: edges plus a seeded spread."""
     g = torch.Generator("cpu").manual_seed(10_000 + seed)
@@ -125,7 +152,17 @@ DECODE = [
 ]
 
 
-def decode_bytes(H, d, seq_lens, elem_bytes=2):
-    """Algorithmic decode bytes: K and V rows actually read, plus q in and out."""
+# Grouped-head decode shaped like a Llama-3-8B layer (32 query heads over 8 K/V heads
+# of 128): a ragged batch of 8 over a 4096-row cache.
+DECODE_GQA = [
+    DecodeCase("decode_gqa_b8_hq32_hkv8_len4096_d128_bf16_ragged", 8, 32, 4096, 128, "bf16", 1 / math.sqrt(128)),
+]
+DECODE_GQA_HKV = {DECODE_GQA[0].name: 8}
+
+
+def decode_bytes(H, d, seq_lens, elem_bytes=2, Hkv=None):
+    """Algorithmic decode bytes: K and V rows actually read (once per K/V head), plus
+    q in and out (once per query head)."""
     B = len(seq_lens)
-    return sum(2 * H * int(L) * d * elem_bytes for L in seq_lens) + 2 * B * H * d * elem_bytes
+    Hkv = H if Hkv is None else Hkv
+    return sum(2 * Hkv * int(L) * d * elem_bytes for L in seq_lens) + 2 * B * H * d * elem_bytes
