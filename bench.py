@@ -16,6 +16,9 @@ Prints ONE JSON line.  `value` is prefill TFLOP/s over the whole timed region
 time).  `roofline` covers the prefill kernel, timed with HIP events on the stream it
 runs on.  `decode` reports the decode path's HBM rate, timed with events after a
 512 MiB read that evicts the L2 and the Infinity Cache before every call.
+`decode_gqa` does the same for grouped K/V heads (B=8, 32 query heads over 8 K/V
+heads of 128, bf16, cache 4096 rows), whose bytes count the cache once per K/V head;
+it runs after the timed steps and is not part of them.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
 """
 
@@ -194,19 +197,41 @@ def main():
     # dirty lines whose write-back then competes with the decode's reads.
     flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     flush_sink = torch.empty((), dtype=torch.int64, device=dev)
-    cold = []
-    for i in range(args.decode_iters):
-        torch.sum(flush, dim=0, out=flush_sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        ea.decode(dq_, dk_, dv_, dl_, scale=D.scale, out=dout, chunk=chunk, workspace=ws)
-        b.record()
-        cold.append((a, b))
-    torch.cuda.synchronize()
-    cold_us = float(np.mean([a.elapsed_time(b) for a, b in cold])) * 1e3
+
+    def cold_us_of(call, iters):
+        cold = []
+        for _ in range(iters):
+            torch.sum(flush, dim=0, out=flush_sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            cold.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in cold])) * 1e3
+
+    cold_us = cold_us_of(lambda: ea.decode(dq_, dk_, dv_, dl_, scale=D.scale, out=dout, chunk=chunk, workspace=ws),
+                         args.decode_iters)
     warm_us = float(np.mean(dec_ms_warm)) * 1e3
     dec_gbs = dec_bytes / (cold_us * 1e-6) / 1e9
     log(f"decode cold {cold_us:.2f} us = {dec_gbs:.0f} GB/s; warm {warm_us:.2f} us")
+
+    # Grouped K/V heads (a wider row than the step: the K/V cache is read once per
+    # group of query heads), timed the same way outside the step.
+    GQ = W.DECODE_GQA[0]
+    gkv = W.DECODE_GQA_HKV[GQ.name]
+    gq, gk, gv, gl = W.decode_inputs_gqa(GQ.B, GQ.H, gkv, GQ.max_len, GQ.d, GQ.dtype, seed=0)
+    gq_, gk_, gv_, gl_ = (t.to(dev) for t in (gq, gk, gv, gl))
+    gout = torch.empty_like(gq_)
+    gchunk, gns = ea.decode_gqa_choose_split(GQ.B, GQ.H, gkv, GQ.max_len, GQ.d, cus)
+    gws = torch.empty(ea.decode_workspace_bytes(GQ.B, GQ.H, gns, GQ.d), dtype=torch.uint8, device=dev)
+    gcall = lambda: ea.decode(gq_, gk_, gv_, gl_, scale=GQ.scale, out=gout, chunk=gchunk, workspace=gws)  # noqa: E731
+    for _ in range(3):
+        gcall()
+    gqa_us = cold_us_of(gcall, args.decode_iters)
+    gqa_bytes = W.decode_bytes(GQ.H, GQ.d, gl.tolist(), Hkv=gkv)
+    gqa_gbs = gqa_bytes / (gqa_us * 1e-6) / 1e9
+    log(f"decode (grouped heads {GQ.H}/{gkv}) cold {gqa_us:.2f} us = {gqa_gbs:.0f} GB/s")
 
     # Parity spot check of this run's outputs against the oracle (sampled rows).
     import oracle
@@ -220,7 +245,9 @@ def main():
         perr = max(perr, float(np.max(np.abs(got - ref))))
     dref = oracle.decode(dq.double().numpy(), dk.double().numpy(), dv.double().numpy(), dl.numpy(), D.scale)
     derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
-    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}")
+    gref = oracle.decode(gq.double().numpy(), gk.double().numpy(), gv.double().numpy(), gl.numpy(), GQ.scale)
+    gerr = float(np.max(np.abs(gout.double().cpu().numpy() - gref)))
+    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}, grouped decode {gerr:.2e}")
 
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
@@ -273,7 +300,18 @@ def main():
             "us_warm": round(warm_us, 3),
             "bytes": dec_bytes,
         },
-        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr},
+        "decode_gqa": {
+            "bound": "hbm",
+            "achieved": round(gqa_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gqa_gbs / PEAK_HBM_GBS, 4),
+            "us_cold": round(gqa_us, 3),
+            "bytes": gqa_bytes,
+            "config": {"B": GQ.B, "Hq": GQ.H, "Hkv": gkv, "max_len": GQ.max_len, "d": GQ.d, "dtype": GQ.dtype,
+                       "seq_lens": gl.tolist(), "chunk": gchunk, "n_split": gns},
+        },
+        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
