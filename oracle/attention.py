@@ -88,6 +88,34 @@ def _rows(qh, kh, vh, rows, causal, scale):
     return _softmax_average(s, vh)
 
 
+def prefill_lse(q, k, causal: bool, scale: float) -> np.ndarray:
+    """Row log-sum-exp of the scaled scores: lse[b, h, i] = log sum_j exp(scale q_i . k_j)
+    over the visible keys j, natural log; returns (B, H, N) float64.
+
+    The normaliser of the softmax in the definition above (its log): the output row
+    equals sum_j exp(scale q_i . k_j - lse_i) v_j.  Computed as m + log(sum exp(s - m))
+    with m the row max, which is the same number without overflow.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d)
+    out = np.empty((B, H, N), dtype=np.float64)
+    keys = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            for r0 in range(0, N, ROW_BLOCK):
+                rows = np.arange(r0, min(N, r0 + ROW_BLOCK))
+                s = float(scale) * (q[b, h, rows] @ k[b, g].T)
+                if causal:  # key j visible to row i iff j <= i
+                    s = np.where(rows[:, None] >= keys[None, :], s, -np.inf)
+                m = np.max(s, axis=1)
+                out[b, h, rows] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+    return out
+
+
 def prefill_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:
     """The same definition for selected rows of one (b, h) only; returns (len(rows), d).
 

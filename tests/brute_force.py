@@ -50,3 +50,21 @@ def decode(q, k_cache, v_cache, seq_lens, scale):
         out.append([[_attend(qh[0], kh[:L], vh[:L], scale)]
                     for qh, kh, vh in zip(qb, _expand(kb, len(qb)), _expand(vb, len(qb)))])
     return out
+
+
+def prefill_lse(q, k, causal, scale):
+    """Row log-sum-exp, natural log: log of the exactly rounded sum of exp(score - top),
+    plus top.  q [B][H][N][d], k [B][Hkv][N][d]; returns [B][H][N]."""
+    out = []
+    for qb, kb in zip(q, k):
+        ob = []
+        for qh, kh in zip(qb, _expand(kb, len(qb))):
+            oh = []
+            for i, qrow in enumerate(qh):
+                n = i + 1 if causal else len(kh)
+                scores = [scale * math.fsum(a * b for a, b in zip(qrow, kr)) for kr in kh[:n]]
+                top = max(scores)
+                oh.append(top + math.log(math.fsum(math.exp(sc - top) for sc in scores)))
+            ob.append(oh)
+        out.append(ob)
+    return out

@@ -317,6 +317,58 @@ def pin_grouped_heads_library_sdpa(O):
         assert np.max(np.abs(got - ref)) <= 1e-12
 
 
+def pin_lse_brute_force(O):
+    """Row log-sum-exp equals brute force (exact sums), multi-head and grouped heads."""
+    r = _rng(40)
+    for (B, Hq, Hkv, N, d) in [(1, 2, 2, 9, 4), (2, 4, 2, 6, 3), (1, 3, 1, 16, 8)]:
+        q = r.standard_normal((B, Hq, N, d)) * 1.5
+        k = r.standard_normal((B, Hkv, N, d))
+        for causal in (False, True):
+            got = O.prefill_lse(q, k, causal, 0.7)
+            ref = np.array(brute_force.prefill_lse(_bf(q), _bf(k), causal, 0.7))
+            assert np.max(np.abs(got - ref)) <= 1e-13, (Hq, Hkv, causal)
+
+
+def pin_lse_closed_forms(O):
+    """Q = 0: every visible key weighs 1, so lse = log(number of visible keys): log N
+    for full rows, log(i + 1) for causal row i.  Causal row 0 sees key 0 alone:
+    lse = scale q_0 . k_0.  One-hot q and k giving score a on one key and 0 on the
+    other n - 1: lse = log(e^a + n - 1)."""
+    r = _rng(41)
+    B, H, N, d = 1, 2, 11, 5
+    k = r.standard_normal((B, H, N, d))
+    q0 = np.zeros((B, H, N, d))
+    assert np.max(np.abs(O.prefill_lse(q0, k, False, 0.9) - np.log(N))) <= 1e-14
+    assert np.max(np.abs(O.prefill_lse(q0, k, True, 0.9) - np.log(np.arange(1, N + 1))[None, None])) <= 1e-14
+    q = r.standard_normal((B, H, N, d))
+    got = O.prefill_lse(q, k, True, 0.9)[:, :, 0]
+    assert np.max(np.abs(got - 0.9 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]))) <= 1e-14
+    n, a = 7, 2.5
+    q1 = np.zeros((1, 1, 1, n))
+    q1[0, 0, 0, 0] = 1.0
+    k1 = np.zeros((1, 1, n, n))
+    k1[0, 0, 3, 0] = a
+    # a single query row against n keys: pad q to n rows and read row n - 1 of the full form
+    qn = np.repeat(q1, n, axis=2)
+    got = O.prefill_lse(qn, k1, False, 1.0)[0, 0, n - 1]
+    assert abs(got - math.log(math.exp(a) + n - 1)) <= 1e-14
+
+
+def pin_lse_reconstructs_output(O):
+    """The output row is sum_j exp(scale q_i . k_j - lse_i) v_j (the normaliser the
+    definition divides by), for full and causal rows."""
+    r = _rng(42)
+    B, H, N, d = 2, 2, 30, 6
+    q, k, v = (r.standard_normal((B, H, N, d)) for _ in range(3))
+    for causal in (False, True):
+        lse = O.prefill_lse(q, k, causal, 0.5)
+        s = 0.5 * np.einsum("bhid,bhjd->bhij", q, k)
+        if causal:
+            s = np.where(np.tril(np.ones((N, N), dtype=bool))[None, None], s, -np.inf)
+        recon = np.einsum("bhij,bhjd->bhid", np.exp(s - lse[..., None]), v)
+        assert np.max(np.abs(recon - O.prefill(q, k, v, causal, 0.5))) <= 1e-12
+
+
 PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -338,4 +390,7 @@ PINS = [
     pin_grouped_heads_brute_force,
     pin_grouped_heads_are_repeated_heads,
     pin_grouped_heads_library_sdpa,
+    pin_lse_brute_force,
+    pin_lse_closed_forms,
+    pin_lse_reconstructs_output,
 ]
