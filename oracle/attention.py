@@ -102,18 +102,29 @@ def prefill_lse(q, k, causal: bool, scale: float) -> np.ndarray:
     Hkv = k.shape[1]
     assert k.shape == (B, Hkv, N, d)
     out = np.empty((B, H, N), dtype=np.float64)
-    keys = np.arange(N)
     for b in range(B):
         for h in range(H):
             g = kv_head(h, H, Hkv)
             for r0 in range(0, N, ROW_BLOCK):
                 rows = np.arange(r0, min(N, r0 + ROW_BLOCK))
-                s = float(scale) * (q[b, h, rows] @ k[b, g].T)
-                if causal:  # key j visible to row i iff j <= i
-                    s = np.where(rows[:, None] >= keys[None, :], s, -np.inf)
-                m = np.max(s, axis=1)
-                out[b, h, rows] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+                out[b, h, rows] = _lse_rows(q[b, h], k[b, g], rows, causal, scale)
     return out
+
+
+def _lse_rows(qh, kh, rows, causal, scale):
+    s = (qh[rows] @ kh.T) * float(scale)
+    if causal:  # key j visible to row i iff j <= i
+        keys = np.arange(kh.shape[0])
+        s = np.where(rows[:, None] >= keys[None, :], s, -np.inf)
+    m = np.max(s, axis=1)
+    return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+
+
+def prefill_lse_rows(q, k, causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:
+    """prefill_lse for selected rows of one (b, h) only; returns (len(rows),)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    g = kv_head(h, q.shape[1], k.shape[1])
+    return _lse_rows(np.asarray(q[b, h], dtype=np.float64), np.asarray(k[b, g], dtype=np.float64), rows, causal, scale)
 
 
 def prefill_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:

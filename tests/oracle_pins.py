@@ -369,6 +369,19 @@ def pin_lse_reconstructs_output(O):
         assert np.max(np.abs(recon - O.prefill(q, k, v, causal, 0.5))) <= 1e-12
 
 
+def pin_lse_rows_matches_lse(O):
+    """Row-sampled log-sum-exp equals the full one (grouped heads, both masks)."""
+    r = _rng(43)
+    q = r.standard_normal((2, 4, 40, 8))
+    k = r.standard_normal((2, 2, 40, 8))
+    for causal in (False, True):
+        full = O.prefill_lse(q, k, causal, 0.6)
+        rows = [0, 5, 39, 17]
+        for h in (0, 1, 3):
+            part = O.prefill_lse_rows(q, k, causal, 0.6, 1, h, rows)
+            assert np.max(np.abs(part - full[1, h, rows])) <= 1e-14
+
+
 PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -393,4 +406,5 @@ PINS = [
     pin_lse_brute_force,
     pin_lse_closed_forms,
     pin_lse_reconstructs_output,
+    pin_lse_rows_matches_lse,
 ]

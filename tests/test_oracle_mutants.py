@@ -26,10 +26,11 @@ MUTATIONS = {
     "decode_values_offset": ("out[b, h] = _softmax_average(s, vc[b, g, :L])", "out[b, h] = _softmax_average(s, vc[b, g, 1:L + 1])"),
     "kv_head_modulo": ("return h // (hq // hkv)", "return h % hkv"),
     "kv_head_last_of_group": ("return h // (hq // hkv)", "return min(hkv - 1, (h + 1) // (hq // hkv))"),
-    "lse_without_max": ("out[b, h, rows] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))", "out[b, h, rows] = np.log(np.sum(np.exp(s - m[:, None]), axis=1))"),
-    "lse_base_two": ("out[b, h, rows] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))", "out[b, h, rows] = m + np.log2(np.sum(np.exp(s - m[:, None]), axis=1))"),
+    "lse_without_max": ("return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))", "return np.log(np.sum(np.exp(s - m[:, None]), axis=1))"),
+    "lse_base_two": ("return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))", "return m + np.log2(np.sum(np.exp(s - m[:, None]), axis=1))"),
     "lse_mask_strict": ("np.where(rows[:, None] >= keys[None, :], s, -np.inf)", "np.where(rows[:, None] > keys[None, :], s, -np.inf)"),
-    "lse_unscaled": ("s = float(scale) * (q[b, h, rows] @ k[b, g].T)", "s = (q[b, h, rows] @ k[b, g].T)"),
+    "lse_unscaled": ("s = (qh[rows] @ kh.T) * float(scale)", "s = (qh[rows] @ kh.T)"),
+    "lse_rows_wrong_head": ("g = kv_head(h, q.shape[1], k.shape[1])\n    return _lse_rows", "g = 0\n    return _lse_rows"),
     "prefill_values_head_zero": ("_rows(q[b, h], k[b, g], v[b, g], rows, causal, scale)", "_rows(q[b, h], k[b, g], v[b, 0], rows, causal, scale)"),
     "split_no_rescale": ("wts = [np.exp(m - M) for m in ms]", "wts = [1.0 for m in ms]"),
     "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
