@@ -38,6 +38,7 @@ EXPORTS = (
     "attn_prefill_gqa",
     "attn_decode_gqa",
     "attn_decode_gqa_choose_split",
+    "attn_prefill_ex",
 )
 
 _lib = None
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_prefill_gqa.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.attn_prefill_gqa.restype = i
+        L.attn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.attn_prefill_ex.restype = i
         L.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
         L.attn_decode_gqa.restype = i
         L.attn_decode_gqa_choose_split.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -122,10 +125,12 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
     """Exact attention for fp16/bf16 GPU tensors q (B, H, N, d) and k, v (B, Hkv, N, d);
     returns out shaped like q.  Hkv < H selects grouped K/V heads (query head h reads
-    K/V head h // (H // Hkv)); Hkv must divide H."""
+    K/V head h // (H // Hkv)); Hkv must divide H.  ``lse``: True allocates and returns
+    (out, lse), or a float32 GPU tensor (B, H, N) to fill; each row's natural-log
+    log-sum-exp of the scaled scores."""
     if q.dim() != 4 or k.dim() != 4:
         raise AttnValueError(ATTN_ERR_INVALID_ARG, "q, k, v must be (batch, heads, seq_len, d)")
     B, H, N, d = q.shape
@@ -139,6 +144,13 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None)
     pk = _dev_tensor(k, "k", q.dtype, (B, Hkv, N, d))
     pv = _dev_tensor(v, "v", q.dtype, (B, Hkv, N, d))
     po = _dev_tensor(out, "out", q.dtype, (B, H, N, d))
+    if lse is not None and lse is not False:
+        lse_t = torch.empty(B, H, N, dtype=torch.float32, device=q.device) if lse is True else lse
+        pl = _dev_tensor(lse_t, "lse", torch.float32, (B, H, N))
+        with torch.cuda.device(q.device):
+            _check(lib().attn_prefill_ex(pq, pk, pv, po, pl, B, H, Hkv, N, d, dt, int(bool(causal)), float(scale),
+                                         _stream(q.device)))
+        return out, lse_t
     with torch.cuda.device(q.device):
         st = _stream(q.device)
         if Hkv == H:

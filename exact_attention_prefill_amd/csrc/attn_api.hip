@@ -12,8 +12,8 @@
 #include "attn.h"
 
 namespace attn {
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
-                          int dt, int causal, float scale, int num_cus, hipStream_t s);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                          int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
                          int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
                          hipStream_t st);
@@ -99,8 +99,8 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_err; }
 
-static int prefill_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Hkv, int N, int d,
-                        int dtype, int causal, float scale, void* stream) {
+static int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
+                        int N, int d, int dtype, int causal, float scale, void* stream) {
   int st;
   if ((st = check_common(B, H, N, d, dtype, scale, "N")) != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
@@ -108,21 +108,32 @@ static int prefill_impl(const void* q, const void* k, const void* v, void* out, 
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
     return st;
   if (out == q || out == k || out == v) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
+  if (lse) {
+    if (((uintptr_t)lse & 3u) != 0) return fail(ATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    if ((void*)lse == q || (void*)lse == k || (void*)lse == v || (void*)lse == out)
+      return fail(ATTN_ERR_INVALID_ARG, "lse must not alias another tensor");
+  }
   int cus = 0;
   if ((st = device_cus(&cus)) != ATTN_OK) return st;
-  hipError_t e = attn::launch_prefill(q, k, v, out, B, H, Hkv, N, d, dtype, causal, scale, cus, (hipStream_t)stream);
+  hipError_t e =
+      attn::launch_prefill(q, k, v, out, lse, B, H, Hkv, N, d, dtype, causal, scale, cus, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
 int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int dtype,
                  int causal, float scale, void* stream) {
-  return prefill_impl(q, k, v, out, B, H, H, N, d, dtype, causal, scale, stream);
+  return prefill_impl(q, k, v, out, nullptr, B, H, H, N, d, dtype, causal, scale, stream);
 }
 
 int attn_prefill_gqa(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
                      int dtype, int causal, float scale, void* stream) {
-  return prefill_impl(q, k, v, out, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
+  return prefill_impl(q, k, v, out, nullptr, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
+}
+
+int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int N,
+                    int d, int dtype, int causal, float scale, void* stream) {
+  return prefill_impl(q, k, v, out, lse, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
 }
 
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {

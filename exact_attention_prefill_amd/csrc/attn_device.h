@@ -20,6 +20,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // acc += A * B for a 32x32 output block and a 16-deep contraction.  Each lane holds
 // eight 16-bit elements of A and of B; the lane -> (row, k) assignment is the

@@ -55,6 +55,7 @@ struct PrefillParams {
   float c;        // |scale| * log2(e) (> 0); log2(e) when scale == 0
   uint32_t qxor;  // 0x80008000 flips Q's sign (scale < 0), else 0
   uint32_t qand;  // 0 zeroes Q (scale == 0), else 0xffffffff
+  float* lse;     // optional [B][H][N] row log-sum-exp (natural log), or null
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -493,10 +494,14 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   }
 
   // Epilogue: O = acc / l.  Lane holds d = 32db + 8a + 4*half + b for a, b in 0..3.
+  // The row's scaled scores satisfy sum_j exp(scale s_j) = 2^m l for the reference m
+  // the row settled on, whatever it is, so its log-sum-exp is (m + log2 l) ln 2.
 #pragma unroll
   for (int cb = 0; cb < QB; ++cb) {
     const float l_tot = xhalf_sum(l_run[cb]);
     const float inv = 1.f / l_tot;
+    if (p.lse && half == 0 && qrow[cb] < N)
+      p.lse[(size_t)bh * N + qrow[cb]] = (m_run[cb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     if (qrow[cb] < N) {
       uint16_t* og = p.o + head_off + (size_t)qrow[cb] * D;
 #pragma unroll
@@ -536,9 +541,10 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
 }
 
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
-                          int dt, int causal, float scale, int num_cus, hipStream_t s) {
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                          int d, int dt, int causal, float scale, int num_cus, hipStream_t s) {
   PrefillParams p;
+  p.lse = lse;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;

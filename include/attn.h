@@ -121,6 +121,16 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
 int attn_prefill_gqa(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
                      int dtype, int causal, float scale, void* stream);
 
+/* attn_prefill_ex: attn_prefill_gqa that can also write each row's log-sum-exp
+ * (page 3, "Future work", lists it with the backward pass, which needs it):
+ *   lse : DEVICE float [B][Hq][N], 4-byte aligned, or NULL for none;
+ *         lse[b][h][i] = log( sum over the keys j visible to row i of
+ *                             exp(scale * q[b][h][i] . k[b][h / (Hq/Hkv)][j]) ), natural log,
+ *         so that out[b][h][i] = sum_j exp(scale q_i . k_j - lse[b][h][i]) v_j.
+ * Allocates nothing.  With lse NULL it is attn_prefill_gqa. */
+int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int N,
+                    int d, int dtype, int causal, float scale, void* stream);
+
 /* attn_decode_gqa: q, out [B][Hq][1][d]; k_cache, v_cache [B][Hkv][max_len][d].
  * chunk / workspace / ws_bytes as for attn_decode_ex (chunk 0: automatic, from
  * attn_decode_gqa_choose_split; workspace NULL with ws_bytes 0: stream-ordered

@@ -191,3 +191,27 @@ def test_gqa_chooser():
         assert ea.decode_gqa_choose_split(8, Hq, Hkv, 4096, 128, 256) == ea.decode_choose_split(8, waves, 4096, 128, 256)
     with pytest.raises(ValueError):
         ea.decode_gqa_choose_split(1, 8, 3, 100, 64, 256)
+
+
+def _prefill_ex(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], lse=P[6], B=1, Hq=4, Hkv=2, N=64, d=128, dt=1, causal=1, scale=0.1,
+             s=None)
+    a.update(kw)
+    return ea.lib().attn_prefill_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                    a["d"], a["dt"], a["causal"], a["scale"], a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(lse=P[6] + 2), ea.ATTN_ERR_ALIGNMENT),
+        (dict(lse=P[3]), ea.ATTN_ERR_INVALID_ARG),  # aliases out
+        (dict(lse=P[0]), ea.ATTN_ERR_INVALID_ARG),  # aliases q
+        (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG),
+        (dict(N=0), ea.ATTN_ERR_INVALID_ARG),
+        (dict(d=64, dt=5), ea.ATTN_ERR_INVALID_ARG),
+    ],
+)
+def test_prefill_ex_validation(kw, status):
+    assert _prefill_ex(**kw) == status
+    assert ea.last_error() != ""
