@@ -4,4 +4,4 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
 the benchmark's CPU-baseline leg, never by the product path.
 """
 
-from .attention import decode, decode_split, kv_head, prefill, prefill_lse, prefill_lse_rows, prefill_rows  # noqa: F401
+from .attention import backward, decode, decode_split, kv_head, prefill, prefill_lse, prefill_lse_rows, prefill_rows  # noqa: F401

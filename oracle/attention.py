@@ -201,3 +201,43 @@ def decode_split(q, k_cache, v_cache, seq_lens, scale: float, chunk: int) -> np.
             den = sum(w * l for w, l in zip(wts, ls))
             out[b, h, 0] = num / den
     return out
+
+
+def backward(q, k, v, dout, causal: bool, scale: float):
+    """Gradients of the loss sum(dout * O) for O = prefill(q, k, v, causal, scale);
+    returns (dq, dk, dv) float64, shaped like q, k, v.
+
+    The chain rule through the definition (page 3, "Future work", asks for the
+    backward pass), per (b, h) with P the row-softmax of S = scale q k^T (masked
+    entries exactly 0):
+      dV = P^T dO;   dP = dO V^T;   dS = P * (dP - rowsum(dP * P));
+      dQ = scale dS K;   dK = scale dS^T Q.
+    rowsum(dP * P) equals rowsum(dO * O), the form the method uses.  With grouped
+    heads, a K/V head's gradient sums those of the query heads that read it.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d) and do.shape == q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    keys = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            s = float(scale) * (q[b, h] @ k[b, g].T)
+            if causal:
+                s = np.where(keys[None, :] <= keys[:, None], s, -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            e = np.exp(s - m)
+            pm = e / np.sum(e, axis=1, keepdims=True)
+            dv[b, g] += pm.T @ do[b, h]
+            dp = do[b, h] @ v[b, g].T
+            ds = pm * (dp - np.sum(dp * pm, axis=1, keepdims=True))
+            dq[b, h] = float(scale) * (ds @ k[b, g])
+            dk[b, g] += float(scale) * (ds.T @ q[b, h])
+    return dq, dk, dv

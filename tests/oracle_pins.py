@@ -382,6 +382,92 @@ def pin_lse_rows_matches_lse(O):
             assert np.max(np.abs(part - full[1, h, rows])) <= 1e-14
 
 
+def pin_backward_finite_differences(O):
+    """The gradients equal central finite differences of sum(dO * prefill(...)) on tiny
+    inputs, for every element of q, k and v (multi-head and grouped, both masks)."""
+    r = _rng(50)
+    eps = 1e-6
+    for (Hq, Hkv) in ((2, 2), (2, 1)):
+        q = r.standard_normal((1, Hq, 4, 3))
+        k, v = r.standard_normal((1, Hkv, 4, 3)), r.standard_normal((1, Hkv, 4, 3))
+        do = r.standard_normal((1, Hq, 4, 3))
+        for causal in (False, True):
+            grads = O.backward(q, k, v, do, causal, 0.8)
+            for which, x in enumerate((q, k, v)):
+                num = np.zeros_like(x)
+                for idx in np.ndindex(x.shape):
+                    xp, xm = x.copy(), x.copy()
+                    xp[idx] += eps
+                    xm[idx] -= eps
+                    args_p = [q, k, v]
+                    args_m = [q, k, v]
+                    args_p[which], args_m[which] = xp, xm
+                    lp = np.sum(do * O.prefill(*args_p, causal, 0.8))
+                    lm = np.sum(do * O.prefill(*args_m, causal, 0.8))
+                    num[idx] = (lp - lm) / (2 * eps)
+                assert np.max(np.abs(grads[which] - num)) <= 1e-7, (Hq, Hkv, causal, which)
+
+
+def pin_backward_library_autograd(O):
+    """Library special case: torch autograd through SDPA in fp64 on the CPU
+    (enable_gqa for grouped heads)."""
+    import torch
+
+    r = _rng(51)
+    for (Hq, Hkv) in ((3, 3), (4, 2)):
+        q = r.standard_normal((2, Hq, 37, 8))
+        k, v = r.standard_normal((2, Hkv, 37, 8)), r.standard_normal((2, Hkv, 37, 8))
+        do = r.standard_normal((2, Hq, 37, 8))
+        for causal in (False, True):
+            Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+            out = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=causal, scale=0.45,
+                                                                   enable_gqa=Hq != Hkv)
+            (out * torch.from_numpy(do)).sum().backward()
+            dq, dk, dv = O.backward(q, k, v, do, causal, 0.45)
+            for got, ref in ((dq, Q.grad), (dk, K.grad), (dv, V.grad)):
+                assert np.max(np.abs(got - ref.numpy())) <= 1e-12, (Hq, Hkv, causal)
+
+
+def pin_backward_invariants(O):
+    """Each softmax row sums to one, so the V gradients sum to the dO rows (full and
+    causal); shifting every key by one vector leaves all gradients unchanged (the rows
+    of dS sum to zero); a zero scale gives zero dQ and dK; with causal masking, a dO
+    that only touches row 0 reaches key 0 alone."""
+    r = _rng(52)
+    B, H, N, d = 2, 2, 20, 5
+    q, k, v, do = (r.standard_normal((B, H, N, d)) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv = O.backward(q, k, v, do, causal, 0.7)
+        assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-12
+        u = r.standard_normal(d)
+        g2 = O.backward(q, k + u, v, do, causal, 0.7)
+        for a, b in zip((dq, dk, dv), g2):
+            assert np.max(np.abs(a - b)) <= 1e-11
+        z = O.backward(q, k, v, do, causal, 0.0)
+        assert np.max(np.abs(z[0])) == 0.0 and np.max(np.abs(z[1])) == 0.0
+    do0 = np.zeros_like(do)
+    do0[:, :, 0] = do[:, :, 0]
+    _, dk0, dv0 = O.backward(q, k, v, do0, True, 0.7)
+    assert np.max(np.abs(dk0[:, :, 1:])) == 0.0 and np.max(np.abs(dv0[:, :, 1:])) == 0.0
+    assert np.max(np.abs(dv0[:, :, 0] - do[:, :, 0])) <= 1e-14
+
+
+def pin_backward_grouped_heads(O):
+    """Grouped heads: dQ equals multi-head dQ on repeated K/V, and dK, dV equal the
+    repeated-head gradients summed over each group."""
+    r = _rng(53)
+    B, Hq, Hkv, N, d = 1, 6, 2, 15, 4
+    g = Hq // Hkv
+    q, do = r.standard_normal((B, Hq, N, d)), r.standard_normal((B, Hq, N, d))
+    k, v = r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hkv, N, d))
+    for causal in (False, True):
+        dq, dk, dv = O.backward(q, k, v, do, causal, 0.5)
+        rq, rk, rv = O.backward(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), do, causal, 0.5)
+        assert np.max(np.abs(dq - rq)) <= 1e-13
+        assert np.max(np.abs(dk - rk.reshape(B, Hkv, g, N, d).sum(axis=2))) <= 1e-13
+        assert np.max(np.abs(dv - rv.reshape(B, Hkv, g, N, d).sum(axis=2))) <= 1e-13
+
+
 PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -407,4 +493,8 @@ PINS = [
     pin_lse_closed_forms,
     pin_lse_reconstructs_output,
     pin_lse_rows_matches_lse,
+    pin_backward_finite_differences,
+    pin_backward_library_autograd,
+    pin_backward_invariants,
+    pin_backward_grouped_heads,
 ]

@@ -31,6 +31,12 @@ MUTATIONS = {
     "lse_mask_strict": ("np.where(rows[:, None] >= keys[None, :], s, -np.inf)", "np.where(rows[:, None] > keys[None, :], s, -np.inf)"),
     "lse_unscaled": ("s = (qh[rows] @ kh.T) * float(scale)", "s = (qh[rows] @ kh.T)"),
     "lse_rows_wrong_head": ("g = kv_head(h, q.shape[1], k.shape[1])\n    return _lse_rows", "g = 0\n    return _lse_rows"),
+    "bwd_no_rowsum_term": ("ds = pm * (dp - np.sum(dp * pm, axis=1, keepdims=True))", "ds = pm * dp"),
+    "bwd_dv_untransposed": ("dv[b, g] += pm.T @ do[b, h]", "dv[b, g] += pm @ do[b, h]"),
+    "bwd_dk_unscaled": ("dk[b, g] += float(scale) * (ds.T @ q[b, h])", "dk[b, g] += (ds.T @ q[b, h])"),
+    "bwd_dq_uses_dst": ("dq[b, h] = float(scale) * (ds @ k[b, g])", "dq[b, h] = float(scale) * (ds.T @ k[b, g])"),
+    "bwd_group_overwrites": ("dk[b, g] += float(scale) * (ds.T @ q[b, h])", "dk[b, g] = float(scale) * (ds.T @ q[b, h])"),
+    "bwd_mask_reversed": ("s = np.where(keys[None, :] <= keys[:, None], s, -np.inf)", "s = np.where(keys[None, :] >= keys[:, None], s, -np.inf)"),
     "prefill_values_head_zero": ("_rows(q[b, h], k[b, g], v[b, g], rows, causal, scale)", "_rows(q[b, h], k[b, g], v[b, 0], rows, causal, scale)"),
     "split_no_rescale": ("wts = [np.exp(m - M) for m in ms]", "wts = [1.0 for m in ms]"),
     "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
