@@ -39,6 +39,8 @@ EXPORTS = (
     "attn_decode_gqa",
     "attn_decode_gqa_choose_split",
     "attn_prefill_ex",
+    "attn_backward",
+    "attn_backward_workspace_bytes",
 )
 
 _lib = None
@@ -83,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_gqa.restype = i
         L.attn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.attn_prefill_ex.restype = i
+        L.attn_backward.argtypes = [vp] * 9 + [i] * 7 + [f, vp, sz, vp]
+        L.attn_backward.restype = i
+        L.attn_backward_workspace_bytes.argtypes = [i, i, i]
+        L.attn_backward_workspace_bytes.restype = sz
         L.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
         L.attn_decode_gqa.restype = i
         L.attn_decode_gqa_choose_split.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -158,6 +164,39 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         else:
             _check(lib().attn_prefill_gqa(pq, pk, pv, po, B, H, Hkv, N, d, dt, int(bool(causal)), float(scale), st))
     return out
+
+
+def backward(q, k, v, out, dout, lse, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for out, lse = prefill(q, k, v, causal, scale, lse=True).
+
+    q, out, dout (B, H, N, d); k, v (B, Hkv, N, d); lse float32 (B, H, N); all GPU tensors.
+    """
+    if q.dim() != 4 or k.dim() != 4:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q, k, v must be (batch, heads, seq_len, d)")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ptrs = [_dev_tensor(t, n, q.dtype, (B, H, N, d)) for t, n in ((q, "q"),)]
+    ptrs += [_dev_tensor(t, n, q.dtype, (B, Hkv, N, d)) for t, n in ((k, "k"), (v, "v"))]
+    ptrs += [_dev_tensor(t, n, q.dtype, (B, H, N, d)) for t, n in ((out, "out"), (dout, "dout"))]
+    ptrs += [_dev_tensor(lse, "lse", torch.float32, (B, H, N))]
+    ptrs += [_dev_tensor(dq, "dq", q.dtype, (B, H, N, d))]
+    ptrs += [_dev_tensor(t, n, q.dtype, (B, Hkv, N, d)) for t, n in ((dk, "dk"), (dv, "dv"))]
+    wp, wb = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    with torch.cuda.device(q.device):
+        _check(lib().attn_backward(*ptrs, B, H, Hkv, N, d, dt, int(bool(causal)), float(scale), wp, wb,
+                                   _stream(q.device)))
+    return dq, dk, dv
+
+
+def backward_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib().attn_backward_workspace_bytes(B, H, N))
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, chunk: int = 0, workspace=None,

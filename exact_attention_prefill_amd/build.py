@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

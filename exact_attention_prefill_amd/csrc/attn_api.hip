@@ -18,6 +18,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
                          int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
                          hipStream_t st);
 int decode_heads_per_wave(int H, int Hkv);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                           int d, int dt, int causal, float scale, hipStream_t s);
 }  // namespace attn
 
 namespace {
@@ -160,6 +163,53 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
   while (c - T >= cmin && pairs * ((max_len + c - 1) / c) < target) c -= T;
   *chunk = (int)c;
   *n_split = (int)((max_len + c - 1) / c);
+  return ok();
+}
+
+size_t attn_backward_workspace_bytes(int B, int Hq, int N) {
+  if (B < 1 || Hq < 1 || N < 1) return 0;
+  return (size_t)B * Hq * N * sizeof(float);
+}
+
+int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int dtype, int causal,
+                  float scale, void* workspace, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_common(B, Hq, N, d, dtype, scale, "N")) != ATTN_OK) return st;
+  if ((st = check_heads(Hq, Hkv)) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(out, "out")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(dq, "dq")) ||
+      (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
+    return st;
+  if (!lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (((uintptr_t)lse & 3u) != 0) return fail(ATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+  const void* ins[] = {q, k, v, out, dout, lse};
+  const void* outs[] = {dq, dk, dv};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o == i) return fail(ATTN_ERR_INVALID_ARG, "a gradient output aliases an input");
+  if (dq == dk || dq == dv || dk == dv) return fail(ATTN_ERR_INVALID_ARG, "gradient outputs must be distinct");
+  if (workspace && !aligned16(workspace)) return fail(ATTN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (!workspace && ws_bytes != 0) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but ws_bytes > 0");
+  const size_t need = attn_backward_workspace_bytes(B, Hq, N);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  bool own = false;
+  if (!workspace) {
+    hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", need, hipGetErrorString(e));
+    own = true;
+  } else if (ws_bytes < need) {
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  }
+  hipError_t e = attn::launch_backward(q, k, v, out, dout, lse, (float*)ws, dq, dk, dv, B, Hq, Hkv, N, d, dtype, causal,
+                                       scale, s);
+  if (own) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

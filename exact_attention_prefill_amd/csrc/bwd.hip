@@ -1,0 +1,482 @@
+// Backward pass of exact attention for gfx950 (CDNA4): dQ, dK, dV of the loss
+// sum(dO * O) for O = softmax(scale Q K^T [causal]) V, the step page 3 lists as
+// future work ("Future work").  The softmax is not stored: every kernel recomputes
+// P = exp(scale q.k - lse) from the row log-sum-exp the forward wrote
+// (attn_prefill_ex), so P is the forward's exact normalised probability.
+//
+//   delta_i = sum_d dO_id O_id                     (pre-pass, one value per row)
+//   dS      = P * (dO V^T - delta)                 (elementwise, rows x keys)
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+//
+// Two matrix-core kernels, no atomics, every output written once:
+//   * dQ: a workgroup owns a block of query rows and streams K/V tiles (the forward's
+//     layout: S^T = K Q^T puts one query row per lane column); dP^T = V dO^T, and
+//     dQ^T += K^T dS^T reads K^T with LDS transpose loads.
+//   * dK, dV: a workgroup owns a block of keys and streams Q/dO tiles with S = Q K^T,
+//     so one key per lane column; dV^T += dO^T P and dK^T += Q^T dS read dO^T and
+//     Q^T with transpose loads.  With grouped heads it loops over the group's query
+//     heads, so a K/V head's gradient sums theirs.
+// Tiles staged through LDS are read both as row operands (ds_read_b128) and through
+// transpose loads, so their 16-byte chunks carry a key that is conflict-free for both
+// (verified with the LDS bank-conflict counter): d = 128: ((r&3)<<2) | ((r>>2)&3);
+// d = 64: (((r>>1)&1)<<2) | ((r>>2)&3).  Tiles read only as row operands keep the
+// forward's K key.  P and dS enter the matrix cores rounded to the input type (RNE),
+// as P does in the forward.
+#include "attn_device.h"
+
+namespace attn {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [B][H][N] natural log
+  float* delta;      // [B][H][N] rowsum(dO * O), written by the pre-pass
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, H, Hkv, g, N;
+  int nblk;     // blocks per head along the kernel's own dimension
+  float c;      // scale * log2(e), signed
+  float scale;  // the softmax scale
+};
+
+namespace bwd_cfg {
+constexpr int BN = 64;  // rows of a streamed tile (keys for dQ, query rows for dK/dV)
+constexpr int NW = 4;   // waves per workgroup, 32 rows (dQ) or keys (dK/dV) each
+}  // namespace bwd_cfg
+
+// Chunk keys of a tile row r (16-byte chunks XOR key).
+template <int D>
+__device__ __forceinline__ int dual_key(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int row_key(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Row operand read (A operand of a 32x32x16 MFMA): lane l gets 16 bytes of tile row
+// (32h + l%32), logical chunk 2ks + l/32.
+template <int D, bool DUAL>
+__device__ __forceinline__ u32x4 row_read(const char* buf, int h, int ks, int lane) {
+  constexpr int RB = 2 * D;
+  const int row = 32 * h + (lane & 31);
+  const int key = DUAL ? dual_key<D>(row & 15) : row_key<D>(row & 15);
+  return lds_read_b128((const uint16_t*)buf, row * RB + (((2 * ks + (lane >> 5)) ^ key) << 4));
+}
+
+// Transposed operand (A operand of (d x rows) = X^T P): for the unit in half h of
+// the tile, 16 rows starting at 32h + 16s, d block db; lane l gets d = 32db + l%32
+// at four rows from each of two transpose loads, in the order the packed P / dS
+// operand (from a 32x32 accumulator) lists its rows.
+template <int D>
+__device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, int lane) {
+  constexpr int RB = 2 * D;
+  const int r = lane & 15, gg = (lane >> 4) & 1, half = lane >> 5;
+  const int rowlo = 4 * half + (r >> 2);
+  const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
+  const int row = 32 * h + 16 * s + rowlo;  // row & 15 == rowlo; the second load reads rows + 8
+  const uint32_t off_lo = row * RB + ((chunk ^ dual_key<D>(rowlo)) << 4) + 8 * (r & 1);
+  const uint32_t off_hi = (row + 8) * RB + ((chunk ^ dual_key<D>(rowlo + 8)) << 4) + 8 * (r & 1);
+  const u32x2 lo = lds_read_tr((const uint16_t*)buf, off_lo);
+  const u32x2 hi = lds_read_tr((const uint16_t*)buf, off_hi);
+  return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Stage one BN-row tile of a [rows][D] tensor into LDS: this wave's share of 1 KiB
+// LDS-direct loads; physical slot sl of row r receives logical chunk sl ^ key(r).
+template <int D, bool DUAL>
+__device__ __forceinline__ void stage_tile(const uint16_t* src, int row0, int rows_total, char* dst, int wave,
+                                           int lane) {
+  using namespace bwd_cfg;
+  constexpr int RB = 2 * D;
+  constexpr int TILE = BN * RB;
+  constexpr int NLD = TILE / 1024 / NW;
+  const int left = rows_total - row0;
+  const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * RB;
+  const u32x4 rs = buffer_rsrc((const char*)src + (size_t)row0 * RB, nrec);
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst) + wave * NLD * 1024);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ci = (wave * NLD + i) * 64 + lane;
+    const int row = ci / (RB / 16), sl = ci % (RB / 16);
+    const int key = DUAL ? dual_key<D>(row & 15) : row_key<D>(row & 15);
+    lds_dma16(rs, row * RB + ((sl ^ key) << 4), l0 + i * 1024);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void pack_unit(const f32x16& x, u32x4 (&pf)[2]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) pf[w >> 2][w & 3] = pack2<DT>(x[2 * w], x[2 * w + 1]);
+}
+
+// ---------------------------------------------------------------------------------
+// delta = rowsum(dO * O), D/8 lanes per row.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const long long total = (long long)p.B * p.H * p.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int seg = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < total) {
+    const u32x4 a = *(const u32x4*)(p.o + row * D + seg * 8);
+    const u32x4 b = *(const u32x4*)(p.dout + row * D + seg * 8);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc = __builtin_fmaf(to_f32<DT>(a[x] & 0xffffu), to_f32<DT>(b[x] & 0xffffu), acc);
+      acc = __builtin_fmaf(to_f32<DT>(a[x] >> 16), to_f32<DT>(b[x] >> 16), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
+  if (row < total && seg == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------
+// dQ: workgroup = 128 query rows of one (b, h); tiles of 64 keys.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using namespace bwd_cfg;
+  constexpr int RB = 2 * D, KS = D / 16, DB = D / 32, BM = 32 * NW;
+  constexpr int TILE = BN * RB;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
+  const int work = xcd * per + min(xcd, rem) + slot;
+  const int bh = __builtin_amdgcn_readfirstlane(work / p.nblk);
+  int qb = __builtin_amdgcn_readfirstlane(work - bh * p.nblk);
+  if (CAUSAL) qb = p.nblk - 1 - qb;
+  const int kvbh = __builtin_amdgcn_readfirstlane(bh / p.g);
+  const int N = p.N;
+  const int q0 = qb * BM, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
+  const bool row_ok = qrow < N;
+  const uint16_t* kg = p.k + (size_t)kvbh * N * D;
+  const uint16_t* vg = p.v + (size_t)kvbh * N * D;
+
+  u32x4 qf[KS], df[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = (u32x4){0, 0, 0, 0};
+    df[ks] = (u32x4){0, 0, 0, 0};
+    if (row_ok) {
+      const size_t off = ((size_t)bh * N + qrow) * D + 16 * ks + 8 * half;
+      qf[ks] = *(const u32x4*)(p.q + off);
+      df[ks] = *(const u32x4*)(p.dout + off);
+    }
+  }
+  const float lse2 = row_ok ? p.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.f;
+
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = (f32x16){};
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kv_end + BN - 1) / BN;
+  const int nu = (kv_end + 31) / 32;
+  const int nu_w = qw0 >= N ? 0 : (CAUSAL ? min(nu, (qw0 + 31) / 32 + 1) : nu);
+
+  if (N % BN != 0) {  // rows past N are never loaded: start from zeros
+    for (int i = tid; i < TILE / 16; i += 64 * NW) {
+      ((u32x4*)kbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)kbuf1)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf1)[i] = (u32x4){0, 0, 0, 0};
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  stage_tile<D, true>(kg, 0, N, kbuf0, wave, lane);
+  stage_tile<D, false>(vg, 0, N, vbuf0, wave, lane);
+  if (nt > 1) {
+    stage_tile<D, true>(kg, BN, N, kbuf1, wave, lane);
+    stage_tile<D, false>(vg, BN, N, vbuf1, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto unit = [&](int u, const char* kb, const char* vb, int h) __attribute__((always_inline)) {
+    f32x16 st = {}, dpt = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      st = mfma32x32x16<DT>(row_read<D, true>(kb, h, ks, lane), qf[ks], st);
+      dpt = mfma32x32x16<DT>(row_read<D, false>(vb, h, ks, lane), df[ks], dpt);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 32 * u + 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool ok = key < N && (!CAUSAL || key <= qrow);
+      const float pr = fast_exp2(p.c * st[i] - lse2);
+      ds[i] = ok ? pr * (dpt[i] - dl) : 0.f;
+    }
+    u32x4 dsf[2];
+    pack_unit<DT>(ds, dsf);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(tr_read<D>(kb, h, s, db, lane), dsf[s], dqa[db]);
+  };
+
+  for (int t = 0; t < nt; ++t) {
+    char* kb = (t & 1) ? kbuf1 : kbuf0;
+    char* vb = (t & 1) ? vbuf1 : vbuf0;
+    if (2 * t < nu_w) unit(2 * t, kb, vb, 0);
+    if (2 * t + 1 < nu_w) unit(2 * t + 1, kb, vb, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < nt) {
+      stage_tile<D, true>(kg, (t + 2) * BN, N, kb, wave, lane);
+      stage_tile<D, false>(vg, (t + 2) * BN, N, vb, wave, lane);
+    }
+  }
+
+  if (row_ok) {
+    uint16_t* og = p.dq + ((size_t)bh * N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w;
+        w[0] = pack2<DT>(dqa[db][4 * a + 0] * p.scale, dqa[db][4 * a + 1] * p.scale);
+        w[1] = pack2<DT>(dqa[db][4 * a + 2] * p.scale, dqa[db][4 * a + 3] * p.scale);
+        *(u32x2*)(og + 32 * db + 8 * a + 4 * half) = w;
+      }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------------
+// dK, dV: workgroup = 128 keys of one (b, kv head); tiles of 64 query rows of each
+// query head of the group.  One wave per SIMD: the two gradient accumulators and the
+// wave's K and V operands need about 300 registers.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using namespace bwd_cfg;
+  constexpr int RB = 2 * D, KS = D / 16, DB = D / 32, BK = 32 * NW;
+  constexpr int TILE = BN * RB;
+  __shared__ __attribute__((aligned(1024))) char qbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char dbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char dbuf1[TILE];
+  __shared__ __attribute__((aligned(256))) float lsebuf[2][BN];
+  __shared__ __attribute__((aligned(256))) float dlbuf[2][BN];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
+  const int work = xcd * per + min(xcd, rem) + slot;
+  const int kvbh = __builtin_amdgcn_readfirstlane(work / p.nblk);
+  const int kblk = __builtin_amdgcn_readfirstlane(work - kvbh * p.nblk);
+  const int b = __builtin_amdgcn_readfirstlane(kvbh / p.Hkv);
+  const int kvh = kvbh - b * p.Hkv;
+  const int N = p.N;
+  const int k0 = kblk * BK, kw0 = k0 + 32 * wave, key = kw0 + l32;
+  const bool key_ok = key < N;
+
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = (u32x4){0, 0, 0, 0};
+    vf[ks] = (u32x4){0, 0, 0, 0};
+    if (key_ok) {
+      const size_t off = ((size_t)kvbh * N + key) * D + 16 * ks + 8 * half;
+      kf[ks] = *(const u32x4*)(p.k + off);
+      vf[ks] = *(const u32x4*)(p.v + off);
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = (f32x16){};
+    dva[db] = (f32x16){};
+  }
+
+  // Query rows that see any of this block's keys: all of them, or (causal) rows from
+  // the block's first key on, in whole 64-row tiles.
+  const int r_start = CAUSAL ? (k0 / BN) * BN : 0;
+  const int nt = k0 >= N ? 0 : (N - r_start + BN - 1) / BN;
+
+  if (N % BN != 0) {
+    for (int i = tid; i < TILE / 16; i += 64 * NW) {
+      ((u32x4*)qbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)qbuf1)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)dbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)dbuf1)[i] = (u32x4){0, 0, 0, 0};
+    }
+    if (tid < 2 * BN) {
+      (&lsebuf[0][0])[tid] = 0.f;
+      (&dlbuf[0][0])[tid] = 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Tile j of query head jh (rows r_start + 64j) into buffer set j & 1.
+  auto stage = [&](int jh, int j, int set) __attribute__((always_inline)) {
+    const int bh = b * p.H + kvh * p.g + jh;
+    const int row0 = r_start + j * BN;
+    stage_tile<D, true>(p.q + (size_t)bh * N * D, row0, N, set ? qbuf1 : qbuf0, wave, lane);
+    stage_tile<D, true>(p.dout + (size_t)bh * N * D, row0, N, set ? dbuf1 : dbuf0, wave, lane);
+    if (wave == 0) {
+      const int left = N - row0;
+      const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * 4;
+      const u32x4 rl = buffer_rsrc(p.lse + (size_t)bh * N + row0, nrec);
+      const u32x4 rd = buffer_rsrc(p.delta + (size_t)bh * N + row0, nrec);
+      lds_dma4(rl, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&lsebuf[set][0])));
+      lds_dma4(rd, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&dlbuf[set][0])));
+    }
+  };
+
+  auto unit = [&](int row0u, const char* qb, const char* dbf, const float* lsv, const float* dlv, int h)
+      __attribute__((always_inline)) {
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16<DT>(row_read<D, true>(qb, h, ks, lane), kf[ks], s);
+      dp = mfma32x32x16<DT>(row_read<D, true>(dbf, h, ks, lane), vf[ks], dp);
+    }
+    f32x16 pm, ds;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int rl = 32 * h + 8 * a + 4 * half;  // tile row of accumulator entries 4a..4a+3
+      const f32x4 l4 = *(const f32x4*)(lsv + rl);
+      const f32x4 d4 = *(const f32x4*)(dlv + rl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * a + e;
+        const int row = row0u + 8 * a + 4 * half + e;
+        const bool ok = key_ok && row < N && (!CAUSAL || key <= row);
+        const float pr = fast_exp2(p.c * s[i] - l4[e] * kLog2e);
+        pm[i] = ok ? pr : 0.f;
+        ds[i] = ok ? pr * (dp[i] - d4[e]) : 0.f;
+      }
+    }
+    u32x4 pf[2], dsf[2];
+    pack_unit<DT>(pm, pf);
+    pack_unit<DT>(ds, dsf);
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mfma32x32x16<DT>(tr_read<D>(dbf, h, si, db, lane), pf[si], dva[db]);
+        dka[db] = mfma32x32x16<DT>(tr_read<D>(qb, h, si, db, lane), dsf[si], dka[db]);
+      }
+  };
+
+  // Every (query head, tile) step is one pass of the double-buffered pipeline:
+  // step n reads set n & 1 and, after the barrier that ends it, loads step n + 2.
+  const int steps = p.g * nt;
+  if (steps > 0) {
+    stage(0, 0, 0);
+    if (steps > 1) stage(1 / nt, 1 % nt, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int n = 0; n < steps; ++n) {
+    const int j = n % nt;
+    const int set = n & 1;
+    const int row0 = r_start + j * BN;
+    const char* qb = set ? qbuf1 : qbuf0;
+    const char* dbf = set ? dbuf1 : dbuf0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row0u = row0 + 32 * h;
+      // the unit's rows all precede this wave's first key: nothing to add (causal)
+      const bool live = !CAUSAL || row0u + 31 >= kw0;
+      if (live) unit(row0u, qb, dbf, &lsebuf[set][0], &dlbuf[set][0], h);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (n + 2 < steps) stage((n + 2) / nt, (n + 2) % nt, set);
+  }
+
+  if (key_ok) {
+    const size_t off = ((size_t)kvbh * N + key) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 wk, wv;
+        wk[0] = pack2<DT>(dka[db][4 * a + 0] * p.scale, dka[db][4 * a + 1] * p.scale);
+        wk[1] = pack2<DT>(dka[db][4 * a + 2] * p.scale, dka[db][4 * a + 3] * p.scale);
+        wv[0] = pack2<DT>(dva[db][4 * a + 0], dva[db][4 * a + 1]);
+        wv[1] = pack2<DT>(dva[db][4 * a + 2], dva[db][4 * a + 3]);
+        *(u32x2*)(p.dk + off + 32 * db + 8 * a + 4 * half) = wk;
+        *(u32x2*)(p.dv + off + 32 * db + 8 * a + 4 * half) = wv;
+      }
+  }
+#endif
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(BwdParams p, hipStream_t s) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const long long rows = (long long)p.B * p.H * p.N;
+  hipLaunchKernelGGL((bwd_delta_kernel<DT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int blk = 32 * bwd_cfg::NW;
+  p.nblk = (p.N + blk - 1) / blk;
+  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.H)),
+                     dim3(64 * bwd_cfg::NW), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.Hkv)),
+                     dim3(64 * bwd_cfg::NW), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                           int d, int dt, int causal, float scale, hipStream_t s) {
+  BwdParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.g = H / Hkv;
+  p.N = N;
+  p.nblk = 0;
+  p.c = scale * kLog2e;
+  p.scale = scale;
+#define ATTN_BW(DT_, D_, C_) \
+  if (dt == DT_ && d == D_ && causal == C_) return launch_bwd_t<DT_, D_, C_>(p, s);
+  ATTN_BW(DT_F16, 64, false)
+  ATTN_BW(DT_F16, 64, true)
+  ATTN_BW(DT_F16, 128, false)
+  ATTN_BW(DT_F16, 128, true)
+  ATTN_BW(DT_BF16, 64, false)
+  ATTN_BW(DT_BF16, 64, true)
+  ATTN_BW(DT_BF16, 128, false)
+  ATTN_BW(DT_BF16, 128, true)
+#undef ATTN_BW
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

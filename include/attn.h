@@ -146,6 +146,26 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, con
  * With Hkv == Hq it equals attn_decode_choose_split.  No HIP call. */
 int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split);
 
+/* Backward pass (page 3, "Future work"): gradients of the loss sum(dout * out) for
+ * out = attn_prefill_ex(q, k, v, causal, scale), given that call's out and lse.
+ *   q, out, dout, dq : [B][Hq][N][d];  k, v, dk, dv : [B][Hkv][N][d] (Hkv divides Hq);
+ *   lse : DEVICE float [B][Hq][N] from attn_prefill_ex (4-byte aligned);
+ *   dq = scale dS K, dk = scale dS^T Q, dv = P^T dout with P the softmax and
+ *   dS = P * (dout v^T - rowsum(dout * out)); with grouped heads dk and dv sum over the
+ *   query heads that read each K/V head.  Outputs are written whole (no accumulation
+ *   into their previous contents) and must not alias an input or each other.
+ *   workspace : DEVICE buffer of at least attn_backward_workspace_bytes(B, Hq, N) bytes
+ *   (16-byte aligned; contents on entry do not matter), or NULL with ws_bytes 0 for a
+ *   stream-ordered allocation.
+ * Same dtype, layout, validation and asynchrony rules as attn_prefill.  Deterministic:
+ * no atomics, every output element written by one wave. */
+int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int dtype, int causal,
+                  float scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* Host-only: workspace bytes of attn_backward (one fp32 per query row). */
+size_t attn_backward_workspace_bytes(int B, int Hq, int N);
+
 /* Host-only: bytes of decode workspace for B*H*n_split partials of (m, l, acc[d]) fp32. */
 size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d);
 

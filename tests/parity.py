@@ -42,3 +42,54 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
             f"first at {idx.tolist()} got {got[tuple(idx[0])]:.6f} ref {ref[tuple(idx[0])]:.6f}"
         )
     return float(err.max())
+
+
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def backward_bounds(q, k, v, dout, causal, scale, lse):
+    """Per-element magnitudes that bound the rounding error of the kernels' gradients
+    (all fp64 arrays; lse from the oracle).  Each gradient is a sum of products whose
+    one rounded factor is P (dV) or dS (dQ, dK), off by at most a relative u; dS also
+    carries the error of delta = rowsum(dO * O) computed from the 16-bit O, at most
+    u * sum_d |dO||O| per row.  Returns (bq, bk, bv) such that
+    |error| <= u |gradient| (the 16-bit output) + 2 u b + fp32 accumulation."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    g = H // Hkv
+    bq = np.zeros_like(q)
+    bk = np.zeros_like(k)
+    bv = np.zeros_like(v)
+    keys = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, h // g], v[b, h // g]
+            s = scale * (q[b, h] @ kh.T)
+            if causal:
+                s = np.where(keys[None, :] <= keys[:, None], s, -np.inf)
+            pm = np.exp(s - lse[b, h][:, None])
+            o = pm @ vh
+            dp = dout[b, h] @ vh.T
+            delta = np.sum(dout[b, h] * o, axis=1, keepdims=True)
+            ds = pm * (dp - delta)
+            ddelta = np.sum(np.abs(dout[b, h]) * np.abs(o), axis=1, keepdims=True)
+            dsb = np.abs(ds) + pm * ddelta
+            bq[b, h] = abs(scale) * (dsb @ np.abs(kh))
+            bk[b, h // g] += abs(scale) * (dsb.T @ np.abs(q[b, h]))
+            bv[b, h // g] += pm.T @ np.abs(dout[b, h])
+    return bq, bk, bv
+
+
+def check_grad(got, ref, bound, dtype, what):
+    """|got - ref| <= u |ref| + 2 u bound + 1e-5 bound + 1e-6 elementwise (see backward_bounds)."""
+    u = UNIT_ROUNDOFF[dtype]
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    err = np.abs(got - ref)
+    gate = u * np.abs(ref) + (2 * u + 1e-5) * bound + 1e-6
+    bad = err > gate
+    if np.any(bad):
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} over the gate; first at {list(i)} "
+                             f"got {got[i]:.6g} ref {ref[i]:.6g} gate {gate[i]:.3g}; max err {err.max():.3e}")
+    return float(err.max())

@@ -215,3 +215,38 @@ def _prefill_ex(**kw):
 def test_prefill_ex_validation(kw, status):
     assert _prefill_ex(**kw) == status
     assert ea.last_error() != ""
+
+
+def _backward(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], dout=P[4], lse=P[5], dq=P[6], dk=P[7], dv=0x30000, B=1, Hq=4, Hkv=2,
+             N=64, d=128, dt=1, causal=0, scale=0.1, ws=None, ws_bytes=0, s=None)
+    a.update(kw)
+    return ea.lib().attn_backward(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                  a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["dt"], a["causal"], a["scale"],
+                                  a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG),
+        (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(lse=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(lse=P[5] + 2), ea.ATTN_ERR_ALIGNMENT),
+        (dict(dq=P[0]), ea.ATTN_ERR_INVALID_ARG),  # gradient aliases q
+        (dict(dv=P[6]), ea.ATTN_ERR_INVALID_ARG),  # dv aliases dq
+        (dict(dout=None), ea.ATTN_ERR_INVALID_ARG),
+        (dict(causal=3), ea.ATTN_ERR_INVALID_ARG),
+        (dict(ws=0x40000, ws_bytes=16), ea.ATTN_ERR_WORKSPACE),
+        (dict(ws=None, ws_bytes=16), ea.ATTN_ERR_INVALID_ARG),
+        (dict(ws=0x40008, ws_bytes=1 << 20), ea.ATTN_ERR_ALIGNMENT),
+    ],
+)
+def test_backward_validation(kw, status):
+    assert _backward(**kw) == status
+    assert ea.last_error() != ""
+
+
+def test_backward_workspace_bytes():
+    assert ea.backward_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert ea.backward_workspace_bytes(0, 8, 100) == 0

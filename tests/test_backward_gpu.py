@@ -1,0 +1,89 @@
+"""Backward pass (attn_backward) on the GPU against the fp64 oracle's gradients.
+
+The gate is elementwise (tests/parity.py, check_grad): the rounding of the 16-bit
+gradient itself plus twice the unit roundoff times a bound built from absolute values
+of the products whose one factor the kernels round (P, dS) and of the delta error."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_prefill_amd as ea
+import oracle
+import workloads as W
+from parity import backward_bounds, check_grad, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_backward(B, Hq, Hkv, N, d, dtype, causal, scale, seed):
+    q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, dtype, seed)
+    g = torch.Generator("cpu").manual_seed(seed + 1000)
+    dout = torch.randn(B, Hq, N, d, generator=g, dtype=torch.float32).to(q.dtype)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=scale, lse=True)
+    dq, dk, dv = ea.backward(qd, kd, vd, out, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (q, k, v, dout), (dq, dk, dv)
+
+
+def parity(B, Hq, Hkv, N, d, dtype, causal, scale, seed):
+    (q, k, v, dout), (dq, dk, dv) = run_backward(B, Hq, Hkv, N, d, dtype, causal, scale, seed)
+    qf, kf, vf, df = (f64(t) for t in (q, k, v, dout))
+    rq, rk, rv = oracle.backward(qf, kf, vf, df, causal, scale)
+    lse = oracle.prefill_lse(qf, kf, causal, scale)
+    bq, bk, bv = backward_bounds(qf, kf, vf, df, causal, scale, lse)
+    what = f"B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} scale={scale:.3g}"
+    check_grad(f64(dq), rq, bq, dtype, "dq " + what)
+    check_grad(f64(dk), rk, bk, dtype, "dk " + what)
+    check_grad(f64(dv), rv, bv, dtype, "dv " + what)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 130, 257])
+def test_backward_parity(N, causal, d, dtype):
+    parity(1, 2, 2, N, d, dtype, causal, 1 / np.sqrt(d), seed=N + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads", [(4, 2), (6, 1), (8, 8)], ids=lambda h: f"hq{h[0]}_hkv{h[1]}")
+def test_backward_grouped_heads(heads, causal):
+    parity(2, heads[0], heads[1], 200, 128, "bf16", causal, 0.0884, seed=heads[0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_many_tiles(d, causal):
+    parity(1, 4, 2, 700, d, "f16" if d == 64 else "bf16", causal, 1 / np.sqrt(d), seed=7)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
+def test_backward_scales(scale):
+    parity(1, 2, 1, 150, 64, "f16", True, scale, seed=11)
+    parity(1, 2, 2, 150, 128, "bf16", False, scale, seed=12)
+
+
+def test_backward_deterministic():
+    a = run_backward(1, 4, 2, 333, 128, "bf16", True, 0.09, 3)[1]
+    b = run_backward(1, 4, 2, 333, 128, "bf16", True, 0.09, 3)[1]
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_workspace_and_errors():
+    (q, k, v, dout), _ = run_backward(1, 2, 2, 100, 64, "f16", False, 0.125, 5)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ea.prefill(qd, kd, vd, scale=0.125, lse=True)
+    ws = torch.full((ea.backward_workspace_bytes(1, 2, 100) // 4,), float("nan"), device=DEV)
+    a = ea.backward(qd, kd, vd, out, dod, lse, scale=0.125, workspace=ws)
+    b = ea.backward(qd, kd, vd, out, dod, lse, scale=0.125)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ea.AttnError) as e:
+        ea.backward(qd, kd, vd, out, dod, lse, scale=0.125, workspace=small)
+    assert e.value.status == ea.ATTN_ERR_WORKSPACE
