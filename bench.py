@@ -19,6 +19,9 @@ runs on.  `decode` reports the decode path's HBM rate, timed with events after a
 `decode_gqa` does the same for grouped K/V heads (B=8, 32 query heads over 8 K/V
 heads of 128, bf16, cache 4096 rows), whose bytes count the cache once per K/V head;
 it runs after the timed steps and is not part of them.
+`backward` times the backward pass (dq, dk, dv from out, lse and a seeded dout) at
+the prefill's shape, also outside the steps; its flop count is 2.5 times the
+forward's (the five products of the chain rule, each of the forward's size).
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
 """
 
@@ -114,6 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--bwd-iters", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument(
@@ -233,6 +237,30 @@ def main():
     gqa_gbs = gqa_bytes / (gqa_us * 1e-6) / 1e9
     log(f"decode (grouped heads {GQ.H}/{gkv}) cold {gqa_us:.2f} us = {gqa_gbs:.0f} GB/s")
 
+    # Backward pass at the prefill's shape (out and lse from the forward with the
+    # log-sum-exp output, a seeded dout), timed with events outside the step.
+    bdo = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=1)[0].to(dev)
+    bout, blse = ea.prefill(q, k, v, causal=P.causal, scale=P.scale, lse=True)
+    bws = torch.empty(ea.backward_workspace_bytes(P.B, P.H, P.N) // 4, dtype=torch.float32, device=dev)
+    bgrads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+
+    def bcall():
+        ea.backward(q, k, v, bout, bdo, blse, causal=P.causal, scale=P.scale, dq=bgrads[0], dk=bgrads[1],
+                    dv=bgrads[2], workspace=bws)
+
+    for _ in range(2):
+        bcall()
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.bwd_iters)]
+    for a, b in bev:
+        a.record()
+        bcall()
+        b.record()
+    torch.cuda.synchronize()
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bev]))
+    bwd_flop = 2.5 * P.flop  # five products of the forward's size (QK^T, dO V^T, dV, dQ, dK)
+    bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    log(f"backward {bwd_ms:.3f} ms = {bwd_tflops:.1f} TFLOP/s")
+
     # Parity spot check of this run's outputs against the oracle (sampled rows).
     import oracle
 
@@ -247,7 +275,12 @@ def main():
     derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
     gref = oracle.decode(gq.double().numpy(), gk.double().numpy(), gv.double().numpy(), gl.numpy(), GQ.scale)
     gerr = float(np.max(np.abs(gout.double().cpu().numpy() - gref)))
-    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}, grouped decode {gerr:.2e}")
+    bdq_rows = oracle.backward_dq_rows(qc[:, :1].double().numpy(), kc[:, :1].double().numpy(),
+                                       vc[:, :1].double().numpy(), bdo[:, :1].double().cpu().numpy(),
+                                       P.causal, P.scale, 0, 0, rows)
+    berr = float(np.max(np.abs(bgrads[0][0, 0, rows].double().cpu().numpy() - bdq_rows)))
+    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}, grouped decode {gerr:.2e}, "
+        f"backward dq sampled {berr:.2e}")
 
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
@@ -311,7 +344,18 @@ def main():
             "config": {"B": GQ.B, "Hq": GQ.H, "Hkv": gkv, "max_len": GQ.max_len, "d": GQ.d, "dtype": GQ.dtype,
                        "seq_lens": gl.tolist(), "chunk": gchunk, "n_split": gns},
         },
-        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr},
+        "backward": {
+            "bound": "mfma",
+            "achieved": round(bwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "ms": round(bwd_ms, 4),
+            "flop": bwd_flop,
+            "config": {"B": P.B, "H": P.H, "N": P.N, "d": P.d, "dtype": P.dtype, "causal": P.causal},
+        },
+        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr,
+                   "backward_dq_sampled_max_err": berr},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

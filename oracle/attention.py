@@ -241,3 +241,51 @@ def backward(q, k, v, dout, causal: bool, scale: float):
             dq[b, h] = float(scale) * (ds @ k[b, g])
             dk[b, g] += float(scale) * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def _head_grads_block(qh, kh, vh, doh, rows, causal, scale):
+    """For a block of query rows of one head: P and dS (the chain rule above, per row;
+    every row's values depend on that row alone).  Returns (pm, ds), each (R, N)."""
+    s = float(scale) * np.matmul(qh[rows], kh.T)
+    if causal:  # key j visible to row i iff j <= i
+        s = np.where(np.arange(kh.shape[0]) <= rows[:, None], s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    pm = e / np.sum(e, axis=1, keepdims=True)
+    dp = doh[rows] @ vh.T
+    ds = pm * (dp - (dp * pm).sum(axis=1, keepdims=True))
+    return pm, ds
+
+
+def backward_dq_rows(q, k, v, dout, causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:
+    """Rows of dq for query head h of batch b (the backward definition above, only the
+    selected rows: dq_i depends on row i's P and dP alone); returns (len(rows), d)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    g = kv_head(h, q.shape[1], k.shape[1])
+    f = lambda t: np.asarray(t, dtype=np.float64)  # noqa: E731
+    kh = f(k[b, g])
+    _, ds = _head_grads_block(f(q[b, h]), kh, f(v[b, g]), f(dout[b, h]), rows, causal, scale)
+    return float(scale) * (ds @ kh)
+
+
+def backward_dkdv_rows(q, k, v, dout, causal: bool, scale: float, b: int, g: int, keys):
+    """Rows ``keys`` of dk and dv for K/V head g of batch b, summed over the query heads
+    that read it (the backward definition above).  Each key row's gradient gathers
+    column j of P and dS over every query row, so every query row is formed, one block
+    of rows at a time; returns (dk, dv), each (len(keys), d)."""
+    keys = np.asarray(keys, dtype=np.int64)
+    f = lambda t: np.asarray(t, dtype=np.float64)  # noqa: E731
+    H, Hkv, N = q.shape[1], k.shape[1], q.shape[2]
+    kh, vh = f(k[b, g]), f(v[b, g])
+    dk = np.zeros((len(keys), kh.shape[1]))
+    dv = np.zeros((len(keys), kh.shape[1]))
+    for h in range(H):
+        if kv_head(h, H, Hkv) != g:
+            continue
+        qh, doh = f(q[b, h]), f(dout[b, h])
+        for r0 in range(0, N, ROW_BLOCK):
+            rows = np.arange(r0, min(N, r0 + ROW_BLOCK))
+            pm, ds = _head_grads_block(qh, kh, vh, doh, rows, causal, scale)
+            dv += pm[:, keys].T @ doh[rows]
+            dk += float(scale) * (ds[:, keys].T @ qh[rows])
+    return dk, dv

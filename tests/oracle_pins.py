@@ -468,6 +468,25 @@ def pin_backward_grouped_heads(O):
         assert np.max(np.abs(dv - rv.reshape(B, Hkv, g, N, d).sum(axis=2))) <= 1e-13
 
 
+def pin_backward_sampled_matches_backward(O):
+    """Row-sampled dq and key-row-sampled dk, dv equal the full backward (grouped heads,
+    both masks, more query rows than one block of rows)."""
+    r = _rng(54)
+    B, Hq, Hkv, N, d = 2, 4, 2, 1100, 3
+    q, do = r.standard_normal((B, Hq, N, d)), r.standard_normal((B, Hq, N, d))
+    k, v = r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hkv, N, d))
+    rows = [0, 1, 517, 1023, 1024, 1099]
+    for causal in (False, True):
+        dq, dk, dv = O.backward(q, k, v, do, causal, 0.6)
+        for h in (0, 3):
+            part = O.backward_dq_rows(q, k, v, do, causal, 0.6, 1, h, rows)
+            assert np.max(np.abs(part - dq[1, h, rows])) <= 1e-13, (causal, h)
+        for g in (0, 1):
+            pk, pv = O.backward_dkdv_rows(q, k, v, do, causal, 0.6, 1, g, rows)
+            assert np.max(np.abs(pk - dk[1, g, rows])) <= 1e-12, (causal, g)
+            assert np.max(np.abs(pv - dv[1, g, rows])) <= 1e-12, (causal, g)
+
+
 PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -497,4 +516,5 @@ PINS = [
     pin_backward_library_autograd,
     pin_backward_invariants,
     pin_backward_grouped_heads,
+    pin_backward_sampled_matches_backward,
 ]

@@ -47,6 +47,21 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
 UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
+def _bound_terms(qh, kh, vh, doh, rows, causal, scale, lse_rows):
+    """For query rows ``rows`` of one head: the softmax P (from the oracle's lse) and
+    |dS| + P * sum_d |dO||O|, the magnitude that bounds the rounded dS and delta terms."""
+    s = scale * (qh[rows] @ kh.T)
+    if causal:
+        s = np.where(np.arange(kh.shape[0])[None, :] <= rows[:, None], s, -np.inf)
+    pm = np.exp(s - lse_rows[:, None])
+    o = pm @ vh
+    dp = doh[rows] @ vh.T
+    delta = np.sum(doh[rows] * o, axis=1, keepdims=True)
+    ds = pm * (dp - delta)
+    ddelta = np.sum(np.abs(doh[rows]) * np.abs(o), axis=1, keepdims=True)
+    return pm, np.abs(ds) + pm * ddelta
+
+
 def backward_bounds(q, k, v, dout, causal, scale, lse):
     """Per-element magnitudes that bound the rounding error of the kernels' gradients
     (all fp64 arrays; lse from the oracle).  Each gradient is a sum of products whose
@@ -60,24 +75,47 @@ def backward_bounds(q, k, v, dout, causal, scale, lse):
     bq = np.zeros_like(q)
     bk = np.zeros_like(k)
     bv = np.zeros_like(v)
-    keys = np.arange(N)
+    rows = np.arange(N)
     for b in range(B):
         for h in range(H):
             kh, vh = k[b, h // g], v[b, h // g]
-            s = scale * (q[b, h] @ kh.T)
-            if causal:
-                s = np.where(keys[None, :] <= keys[:, None], s, -np.inf)
-            pm = np.exp(s - lse[b, h][:, None])
-            o = pm @ vh
-            dp = dout[b, h] @ vh.T
-            delta = np.sum(dout[b, h] * o, axis=1, keepdims=True)
-            ds = pm * (dp - delta)
-            ddelta = np.sum(np.abs(dout[b, h]) * np.abs(o), axis=1, keepdims=True)
-            dsb = np.abs(ds) + pm * ddelta
+            pm, dsb = _bound_terms(q[b, h], kh, vh, dout[b, h], rows, causal, scale, lse[b, h])
             bq[b, h] = abs(scale) * (dsb @ np.abs(kh))
             bk[b, h // g] += abs(scale) * (dsb.T @ np.abs(q[b, h]))
             bv[b, h // g] += pm.T @ np.abs(dout[b, h])
     return bq, bk, bv
+
+
+def backward_bounds_rows(q, k, v, dout, causal, scale, b, h, rows):
+    """backward_bounds' bq at query rows ``rows`` of head h of batch b (fp64 inputs)."""
+    import oracle
+
+    rows = np.asarray(rows, dtype=np.int64)
+    g = q.shape[1] // k.shape[1]
+    kh, vh = k[b, h // g], v[b, h // g]
+    lse = oracle.prefill_lse_rows(q, k, causal, scale, b, h, rows)
+    _, dsb = _bound_terms(q[b, h], kh, vh, dout[b, h], rows, causal, scale, lse)
+    return abs(scale) * (dsb @ np.abs(kh))
+
+
+def backward_bounds_keys(q, k, v, dout, causal, scale, b, kv, keys, block=1024):
+    """backward_bounds' bk, bv at key rows ``keys`` of K/V head kv of batch b."""
+    import oracle
+
+    keys = np.asarray(keys, dtype=np.int64)
+    H, N = q.shape[1], q.shape[2]
+    g = H // k.shape[1]
+    kh, vh = k[b, kv], v[b, kv]
+    bk = np.zeros((len(keys), k.shape[3]))
+    bv = np.zeros((len(keys), k.shape[3]))
+    for h in range(kv * g, (kv + 1) * g):
+        for r0 in range(0, N, block):
+            rows = np.arange(r0, min(N, r0 + block))
+            lse = oracle.prefill_lse_rows(q, k, causal, scale, b, h, rows)
+            pm, dsb = _bound_terms(q[b, h], kh, vh, dout[b, h], rows, causal, scale, lse)
+            bk += abs(scale) * (dsb[:, keys].T @ np.abs(q[b, h, rows]))
+            bv += pm[:, keys].T @ np.abs(dout[b, h, rows])
+    return bk, bv
 
 
 def check_grad(got, ref, bound, dtype, what):

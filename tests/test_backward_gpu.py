@@ -87,3 +87,32 @@ def test_backward_workspace_and_errors():
     with pytest.raises(ea.AttnError) as e:
         ea.backward(qd, kd, vd, out, dod, lse, scale=0.125, workspace=small)
     assert e.value.status == ea.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_headline_sampled(causal):
+    """The forward's headline shape (B=1, H=16, N=16384, d=128, bf16), in the launch
+    configuration the benchmark times: dq at sampled query rows and dk, dv at sampled
+    key rows of the first and last heads against the row-sampled oracle."""
+    from parity import backward_bounds_keys, backward_bounds_rows
+
+    P = W.HEADLINE
+    q, k, v = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=0)
+    dout = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=1)[0]
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=P.scale, lse=True)
+    dq, dk, dv = ea.backward(qd, kd, vd, out, dod, lse, causal=causal, scale=P.scale)
+    torch.cuda.synchronize()
+    rows = W.prefill_rows_sample(P.N, 12, seed=2)
+    qf, kf, vf, df = (f64(t[:, [0, P.H - 1]]) for t in (q, k, v, dout))
+    for i, h in enumerate((0, P.H - 1)):
+        what = f"headline causal={causal} h={h}"
+        ref = oracle.backward_dq_rows(qf, kf, vf, df, causal, P.scale, 0, i, rows)
+        bq = backward_bounds_rows(qf, kf, vf, df, causal, P.scale, 0, i, rows)
+        check_grad(f64(dq[0, h, rows]), ref, bq, P.dtype, "dq " + what)
+        rk, rv = oracle.backward_dkdv_rows(qf, kf, vf, df, causal, P.scale, 0, i, rows)
+        bk, bv = backward_bounds_keys(qf, kf, vf, df, causal, P.scale, 0, i, rows)
+        check_grad(f64(dk[0, h, rows]), rk, bk, P.dtype, "dk " + what)
+        check_grad(f64(dv[0, h, rows]), rv, bv, P.dtype, "dv " + what)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()

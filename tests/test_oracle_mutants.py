@@ -37,6 +37,10 @@ MUTATIONS = {
     "bwd_dq_uses_dst": ("dq[b, h] = float(scale) * (ds @ k[b, g])", "dq[b, h] = float(scale) * (ds.T @ k[b, g])"),
     "bwd_group_overwrites": ("dk[b, g] += float(scale) * (ds.T @ q[b, h])", "dk[b, g] = float(scale) * (ds.T @ q[b, h])"),
     "bwd_mask_reversed": ("s = np.where(keys[None, :] <= keys[:, None], s, -np.inf)", "s = np.where(keys[None, :] >= keys[:, None], s, -np.inf)"),
+    "bwd_rows_no_rowsum_term": ("ds = pm * (dp - (dp * pm).sum(axis=1, keepdims=True))", "ds = pm * dp"),
+    "bwd_rows_mask_strict": ("np.where(np.arange(kh.shape[0]) <= rows[:, None]", "np.where(np.arange(kh.shape[0]) < rows[:, None]"),
+    "bwd_rows_one_head_per_group": ("if kv_head(h, H, Hkv) != g:", "if h != g:"),
+    "bwd_rows_dk_unscaled": ("dk += float(scale) * (ds[:, keys].T @ qh[rows])", "dk += ds[:, keys].T @ qh[rows]"),
     "prefill_values_head_zero": ("_rows(q[b, h], k[b, g], v[b, g], rows, causal, scale)", "_rows(q[b, h], k[b, g], v[b, 0], rows, causal, scale)"),
     "split_no_rescale": ("wts = [np.exp(m - M) for m in ms]", "wts = [1.0 for m in ms]"),
     "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
