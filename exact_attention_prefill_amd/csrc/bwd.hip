@@ -22,6 +22,8 @@
 // d = 64: (((r>>1)&1)<<2) | ((r>>2)&3).  Tiles read only as row operands keep the
 // forward's K key.  P and dS enter the matrix cores rounded to the input type (RNE),
 // as P does in the forward.
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -262,20 +264,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------------
 // dK, dV: workgroup = 128 keys of one (b, kv head); tiles of 64 query rows of each
-// query head of the group.  One wave per SIMD: the two gradient accumulators and the
-// wave's K and V operands need about 300 registers.
+// query head of the group, a unit being one 32-row half of a tile.  One wave per
+// SIMD (the two gradient accumulators and the wave's K and V operands need about 300
+// registers), so the wave overlaps its own work with a three-stage pipeline over
+// units, as the forward does:
+//   matrix cores: S_{v+2} = Q K^T and dP_{v+2} = dO V^T  interleaved with
+//                 dV^T += dO_v^T P_v and dK^T += Q_v^T dS_v;
+//   VALU:         P_{v+1} = 2^(c S - lse log2 e), dS_{v+1} = P (dP - delta), rounded.
+// Unit v reads tile v/2, so each pipeline step reads two tiles: three LDS tile sets
+// rotate, and the loads of a tile are issued two pipeline steps before it is read.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using namespace bwd_cfg;
   constexpr int RB = 2 * D, KS = D / 16, DB = D / 32, BK = 32 * NW;
   constexpr int TILE = BN * RB;
-  __shared__ __attribute__((aligned(1024))) char qbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) char qbuf1[TILE];
-  __shared__ __attribute__((aligned(1024))) char dbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) char dbuf1[TILE];
-  __shared__ __attribute__((aligned(256))) float lsebuf[2][BN];
-  __shared__ __attribute__((aligned(256))) float dlbuf[2][BN];
+  constexpr int NS = 3;       // tile sets in LDS
+  constexpr int M = 2 * KS;   // issue slots per pipeline step: one S/dP and one dV/dK MFMA each
+  constexpr int EPS = 16 / M; // softmax-gradient elements per slot
+  constexpr int PF = 2;       // operand prefetch distance in slots
+  constexpr int R = PF + 1;   // operand ring size
+  __shared__ __attribute__((aligned(1024))) char qbuf[NS][TILE];
+  __shared__ __attribute__((aligned(1024))) char dbuf[NS][TILE];
+  __shared__ __attribute__((aligned(256))) float lsebuf[NS][BN];
+  __shared__ __attribute__((aligned(256))) float dlbuf[NS][BN];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -313,28 +325,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // the block's first key on, in whole 64-row tiles.
   const int r_start = CAUSAL ? (k0 / BN) * BN : 0;
   const int nt = k0 >= N ? 0 : (N - r_start + BN - 1) / BN;
+  const int steps = p.g * nt;  // tiles, over the group's query heads in turn
 
-  if (N % BN != 0) {
-    for (int i = tid; i < TILE / 16; i += 64 * NW) {
-      ((u32x4*)qbuf0)[i] = (u32x4){0, 0, 0, 0};
-      ((u32x4*)qbuf1)[i] = (u32x4){0, 0, 0, 0};
-      ((u32x4*)dbuf0)[i] = (u32x4){0, 0, 0, 0};
-      ((u32x4*)dbuf1)[i] = (u32x4){0, 0, 0, 0};
+  if (N % BN != 0) {  // rows past N are never loaded: every set starts from zeros
+    for (int i = tid; i < NS * TILE / 16; i += 64 * NW) {
+      ((u32x4*)&qbuf[0][0])[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)&dbuf[0][0])[i] = (u32x4){0, 0, 0, 0};
     }
-    if (tid < 2 * BN) {
-      (&lsebuf[0][0])[tid] = 0.f;
-      (&dlbuf[0][0])[tid] = 0.f;
+    for (int i = tid; i < NS * BN; i += 64 * NW) {
+      (&lsebuf[0][0])[i] = 0.f;
+      (&dlbuf[0][0])[i] = 0.f;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  // Tile j of query head jh (rows r_start + 64j) into buffer set j & 1.
-  auto stage = [&](int jh, int j, int set) __attribute__((always_inline)) {
+  // Tile n of the flattened (query head, row tile) order into set n % NS.
+  auto stage = [&](int n) __attribute__((always_inline)) {
+    const int jh = n / nt, j = n - jh * nt, set = n % NS;
     const int bh = b * p.H + kvh * p.g + jh;
     const int row0 = r_start + j * BN;
-    stage_tile<D, true>(p.q + (size_t)bh * N * D, row0, N, set ? qbuf1 : qbuf0, wave, lane);
-    stage_tile<D, true>(p.dout + (size_t)bh * N * D, row0, N, set ? dbuf1 : dbuf0, wave, lane);
+    stage_tile<D, true>(p.q + (size_t)bh * N * D, row0, N, qbuf[set], wave, lane);
+    stage_tile<D, true>(p.dout + (size_t)bh * N * D, row0, N, dbuf[set], wave, lane);
     if (wave == 0) {
       const int left = N - row0;
       const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * 4;
@@ -344,68 +356,172 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       lds_dma4(rd, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&dlbuf[set][0])));
     }
   };
+  auto row0_of = [&](int n) __attribute__((always_inline)) { return r_start + (n % nt) * BN; };
 
-  auto unit = [&](int row0u, const char* qb, const char* dbf, const float* lsv, const float* dlv, int h)
+  // Softmax gradient of one unit, element by element.  Accumulator entry i of lane l
+  // is (row 8(i/4) + 4(l/32) + i%4 of the unit, key l%32).  Rows past N and (causal)
+  // rows before the key get x = -inf, so P = 0 and dS = 0 exactly.
+  const int kk = CAUSAL ? key : 0;
+  const uint32_t lim = (uint32_t)(N - kk);
+  struct GradIn {
+    const float* lse;
+    const float* dl;
+    int rb;  // unit row of entry 0 for this lane half, minus kk
+  };
+  auto grad_in = [&](int n, int hb) __attribute__((always_inline)) {
+    const int set = n % NS;
+    GradIn g;
+    g.lse = &lsebuf[set][32 * hb];
+    g.dl = &dlbuf[set][32 * hb];
+    g.rb = row0_of(n) + 32 * hb + 4 * half - kk;
+    return g;
+  };
+  auto grad_rows = [&](const GradIn& g, int a, f32x4& l4, f32x4& d4) __attribute__((always_inline)) {
+    l4 = *(const f32x4*)(g.lse + 8 * a + 4 * half);
+    d4 = *(const f32x4*)(g.dl + 8 * a + 4 * half);
+  };
+  auto grad_elem = [&](const GradIn& g, const f32x16& s, const f32x16& dp, const f32x4& l4, const f32x4& d4,
+                       int i, float& pm, float& ds) __attribute__((always_inline)) {
+    const int e = i & 3;
+    const bool ok = (uint32_t)(g.rb + 8 * (i >> 2) + e) < lim;
+    float x = __builtin_fmaf(s[i], p.c, -l4[e] * kLog2e);
+    x = ok ? x : -INFINITY;
+    pm = fast_exp2(x);
+    ds = pm * (dp[i] - d4[e]);
+  };
+  // The whole unit at once (the pipeline prologue).
+  auto grad_unit = [&](const GradIn& g, const f32x16& s, const f32x16& dp, u32x4 (&pf)[2], u32x4 (&dsf)[2])
       __attribute__((always_inline)) {
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16<DT>(row_read<D, true>(qb, h, ks, lane), kf[ks], s);
-      dp = mfma32x32x16<DT>(row_read<D, true>(dbf, h, ks, lane), vf[ks], dp);
-    }
-    f32x16 pm, ds;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int rl = 32 * h + 8 * a + 4 * half;  // tile row of accumulator entries 4a..4a+3
-      const f32x4 l4 = *(const f32x4*)(lsv + rl);
-      const f32x4 d4 = *(const f32x4*)(dlv + rl);
+      f32x4 l4, d4;
+      grad_rows(g, a, l4, d4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * a + e;
-        const int row = row0u + 8 * a + 4 * half + e;
-        const bool ok = key_ok && row < N && (!CAUSAL || key <= row);
-        const float pr = fast_exp2(p.c * s[i] - l4[e] * kLog2e);
-        pm[i] = ok ? pr : 0.f;
-        ds[i] = ok ? pr * (dp[i] - d4[e]) : 0.f;
+      for (int e = 0; e < 4; e += 2) {
+        float p0, d0, p1, d1;
+        grad_elem(g, s, dp, l4, d4, 4 * a + e, p0, d0);
+        grad_elem(g, s, dp, l4, d4, 4 * a + e + 1, p1, d1);
+        const int w = 2 * a + e / 2;
+        pf[w >> 2][w & 3] = pack2<DT>(p0, p1);
+        dsf[w >> 2][w & 3] = pack2<DT>(d0, d1);
       }
     }
-    u32x4 pf[2], dsf[2];
-    pack_unit<DT>(pm, pf);
-    pack_unit<DT>(ds, dsf);
-#pragma unroll
-    for (int si = 0; si < 2; ++si)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32x32x16<DT>(tr_read<D>(dbf, h, si, db, lane), pf[si], dva[db]);
-        dka[db] = mfma32x32x16<DT>(tr_read<D>(qb, h, si, db, lane), dsf[si], dka[db]);
-      }
   };
 
-  // Every (query head, tile) step is one pass of the double-buffered pipeline:
-  // step n reads set n & 1 and, after the barrier that ends it, loads step n + 2.
-  const int steps = p.g * nt;
-  if (steps > 0) {
-    stage(0, 0, 0);
-    if (steps > 1) stage(1 / nt, 1 % nt, 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int n = 0; n < steps; ++n) {
-    const int j = n % nt;
-    const int set = n & 1;
-    const int row0 = r_start + j * BN;
-    const char* qb = set ? qbuf1 : qbuf0;
-    const char* dbf = set ? dbuf1 : dbuf0;
+  // Operands: S/dP MFMA i reads row operand i (Q for even i, dO for odd, chunk i/2);
+  // dV/dK MFMA i reads transposed operand i (dO for even i, Q for odd; si = i/(2DB),
+  // db = (i/2) % DB).  Both are read PF slots ahead into rings that span the two
+  // pipeline steps of a tile (operand j of step h sits at (hM + j) mod R).
+  auto a_read = [&](const char* qb, const char* dbb, int h, int i) __attribute__((always_inline)) {
+    return row_read<D, true>((i & 1) ? dbb : qb, h, i >> 1, lane);
+  };
+  auto c_read = [&](const char* qb, const char* dbb, int h, int i) __attribute__((always_inline)) {
+    return tr_read<D>((i & 1) ? qb : dbb, h, (i >> 1) / DB, (i >> 1) % DB, lane);
+  };
+
+  f32x16 sacc[2], dpacc[2];  // S, dP of the units in flight (by unit parity)
+  u32x4 pk[2][2], dsk[2][2]; // packed P, dS of the units in flight (by unit parity)
+
+  // One pipeline step (unit v = 2n + h of tile n, tile n in set SC): A = S/dP of unit
+  // v + 2 (tile n + 1, half h), B = P/dS of unit v + 1 (tile n + h, half 1 - h), C =
+  // dV/dK of unit v (tile n, half h).  The set indices are compile-time so that every
+  // LDS read folds its set into the instruction's offset.  In the last tile, A and B
+  // work on a set that holds no tile of this workgroup's range: their results are
+  // never consumed.
+  auto step = [&](auto h_c, auto sc_c, int n, u32x4 (&ar)[R], u32x4 (&cr)[R]) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    constexpr int SC = decltype(sc_c)::value, SA = (SC + 1) % NS, SB = h == 0 ? SC : SA;
+    const char* qc = qbuf[SC];
+    const char* dc = dbuf[SC];
+    const char* qa = qbuf[SA];
+    const char* da = dbuf[SA];
+    GradIn gi;
+    gi.lse = &lsebuf[SB][32 * (1 - h)];
+    gi.dl = &dlbuf[SB][32 * (1 - h)];
+    gi.rb = row0_of(n + h) + 32 * (1 - h) + 4 * half - kk;
+    f32x16& sn = sacc[h];
+    f32x16& dpn = dpacc[h];
+    const f32x16& sb = sacc[1 - h];
+    const f32x16& dpb = dpacc[1 - h];
+    f32x4 l4[2], d4[2];  // row groups a and a + 1 (by parity of a)
+    grad_rows(gi, 0, l4[0], d4[0]);
+    grad_rows(gi, 1, l4[1], d4[1]);
+    float pe[EPS], de[EPS];
+    float pp = 0.f, dpp = 0.f;  // the even element of a pair, waiting for its partner
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row0u = row0 + 32 * h;
-      // the unit's rows all precede this wave's first key: nothing to add (causal)
-      const bool live = !CAUSAL || row0u + 31 >= kw0;
-      if (live) unit(row0u, qb, dbf, &lsebuf[set][0], &dlbuf[set][0], h);
+    for (int i = 0; i < M; ++i) {
+      const int j = h * M + i;
+      if (i + PF < M) ar[(j + PF) % R] = a_read(qa, da, h, i + PF);
+      else if (h == 0) ar[(j + PF) % R] = a_read(qa, da, 1, i + PF - M);
+      const int ks = i >> 1;
+      if (i & 1) dpn = mfma32x32x16<DT>(ar[j % R], vf[ks], ks == 0 ? (f32x16){} : dpn);
+      else sn = mfma32x32x16<DT>(ar[j % R], kf[ks], ks == 0 ? (f32x16){} : sn);
+      if (i + PF < M) cr[(j + PF) % R] = c_read(qc, dc, h, i + PF);
+      else if (h == 0) cr[(j + PF) % R] = c_read(qc, dc, 1, i + PF - M);
+      const int si = (i >> 1) / DB, db = (i >> 1) % DB;
+      if (i & 1) dka[db] = mfma32x32x16<DT>(cr[j % R], dsk[h][si], dka[db]);
+      else dva[db] = mfma32x32x16<DT>(cr[j % R], pk[h][si], dva[db]);
+#pragma unroll
+      for (int q = 0; q < EPS; ++q) {
+        const int e = EPS * i + q;
+        grad_elem(gi, sb, dpb, l4[(e >> 2) & 1], d4[(e >> 2) & 1], e, pe[q], de[q]);
+        if (e & 1) {
+          const int w = e >> 1;
+          pk[1 - h][w >> 2][w & 3] = pack2<DT>(EPS == 1 ? pp : pe[q - 1], pe[q]);
+          dsk[1 - h][w >> 2][w & 3] = pack2<DT>(EPS == 1 ? dpp : de[q - 1], de[q]);
+        } else if (EPS == 1) {
+          pp = pe[q];
+          dpp = de[q];
+        }
+        if ((e & 3) == 3 && e < 8) grad_rows(gi, (e >> 2) + 2, l4[(e >> 2) & 1], d4[(e >> 2) & 1]);
+      }
+      // Anchor the slot's VALU results in the slot (IR-level code motion ignores
+      // sched_barrier and would gather the softmax gradient after the MFMAs).
+      asm volatile("" ::"v"(pp), "v"(dpp), "v"(pe[0]), "v"(de[0]));
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Tile n (in set SC): its two pipeline steps, then the barrier that frees set SC
+  // for tile n + 3.
+  auto tile = [&](auto sc_c, int n) __attribute__((always_inline)) {
+    constexpr int SC = decltype(sc_c)::value, SA = (SC + 1) % NS;
+    u32x4 ar[R], cr[R];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      ar[i] = a_read(qbuf[SA], dbuf[SA], 0, i);
+      cr[i] = c_read(qbuf[SC], dbuf[SC], 0, i);
+    }
+    step(std::integral_constant<int, 0>(), sc_c, n, ar, cr);
+    step(std::integral_constant<int, 1>(), sc_c, n, ar, cr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (n + 2 < steps) stage((n + 2) / nt, (n + 2) % nt, set);
+    if (n + 3 < steps) stage(n + 3);
+  };
+
+  if (steps > 0) {
+    // Prologue: tiles 0 and 1 in; S/dP of units 0 and 1; P/dS of unit 0; tile 2 in flight.
+    stage(0);
+    if (steps > 1) stage(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (steps > 2) stage(2);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32x32x16<DT>(row_read<D, true>(qbuf[0], hh, ks, lane), kf[ks], s);
+        dp = mfma32x32x16<DT>(row_read<D, true>(dbuf[0], hh, ks, lane), vf[ks], dp);
+      }
+      sacc[hh] = s;
+      dpacc[hh] = dp;
+    }
+    grad_unit(grad_in(0, 0), sacc[0], dpacc[0], pk[0], dsk[0]);
+    for (int n = 0; n < steps; n += NS) {
+      tile(std::integral_constant<int, 0>(), n);
+      if (n + 1 < steps) tile(std::integral_constant<int, 1>(), n + 1);
+      if (n + 2 < steps) tile(std::integral_constant<int, 2>(), n + 2);
+    }
   }
 
   if (key_ok) {
