@@ -22,6 +22,8 @@ it runs after the timed steps and is not part of them.
 `backward` times the backward pass (dq, dk, dv from out, lse and a seeded dout) at
 the prefill's shape, also outside the steps; its flop count is 2.5 times the
 forward's (the five products of the chain rule, each of the forward's size).
+`head_sizes` times the prefill at d = 32, 64, 96, 128 and 256 with the headline's
+B, H and N (bf16, non-causal), outside the steps.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
 """
 
@@ -118,6 +120,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=100)
     ap.add_argument("--bwd-iters", type=int, default=10)
+    ap.add_argument("--no-head-sizes", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument(
@@ -261,6 +264,27 @@ def main():
     bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
     log(f"backward {bwd_ms:.3f} ms = {bwd_tflops:.1f} TFLOP/s")
 
+    # Prefill at every head size the library builds, at the headline's B, H and N
+    # (bf16, non-causal; flop 4*B*H*N*N*d), timed with events outside the step.
+    head_sizes = {}
+    if not args.no_head_sizes:
+        for hd in (32, 64, 96, 128, 256):
+            hq, hk, hv = (t.to(dev) for t in W.prefill_inputs(P.B, P.H, P.N, hd, "bf16", seed=0))
+            hout = torch.empty_like(hq)
+            for _ in range(2):
+                ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
+            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, b in hev:
+                a.record()
+                ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
+                b.record()
+            torch.cuda.synchronize()
+            hms = float(np.mean([a.elapsed_time(b) for a, b in hev]))
+            htf = 4.0 * P.B * P.H * P.N * P.N * hd / (hms * 1e-3) / 1e12
+            head_sizes[str(hd)] = {"ms": round(hms, 4), "tflops": round(htf, 1), "frac": round(htf / PEAK_BF16_TFLOPS, 4)}
+            del hq, hk, hv, hout
+        log("head sizes: " + ", ".join(f"d={k} {v['tflops']} TF" for k, v in head_sizes.items()))
+
     # Parity spot check of this run's outputs against the oracle (sampled rows).
     import oracle
 
@@ -354,6 +378,7 @@ def main():
             "flop": bwd_flop,
             "config": {"B": P.B, "H": P.H, "N": P.N, "d": P.d, "dtype": P.dtype, "causal": P.causal},
         },
+        "head_sizes": {"config": f"prefill B={P.B} H={P.H} N={P.N} bf16 non-causal", "by_d": head_sizes},
         "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr,
                    "backward_dq_sampled_max_err": berr},
         "cpu_baseline": cpu,

@@ -42,11 +42,14 @@ int ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
+
 int check_common(int B, int H, int rows, int d, int dtype, float scale, const char* rows_name) {
   if (B < 1 || H < 1 || rows < 1)
     return fail(ATTN_ERR_INVALID_ARG, "B=%d, H=%d and %s=%d must all be >= 1", B, H, rows_name, rows);
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "dtype %d is not ATTN_F16/ATTN_BF16", dtype);
-  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (64 or 128)", d);
+  if (!head_dim_ok(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
   if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
   // Element offsets are formed in 64 bits, but per-head row counts and grid sizes stay in int.
   const long long elems = (long long)B * H * rows;
@@ -142,7 +145,8 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, floa
 int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {
   if (B < 1 || H < 1 || max_len < 1 || num_cus < 1)
     return fail(ATTN_ERR_INVALID_ARG, "B, H, max_len and num_cus must be >= 1");
-  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (64 or 128)", d);
+  if (!head_dim_ok(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
   if (!chunk || !n_split) return fail(ATTN_ERR_INVALID_ARG, "chunk and n_split must be non-NULL host pointers");
   const long long T = ATTN_DECODE_ROW_GRANULE;
   const long long pairs = (long long)B * H;
@@ -176,6 +180,8 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
                   float scale, void* workspace, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_common(B, Hq, N, d, dtype, scale, "N")) != ATTN_OK) return st;
+  if (d != 64 && d != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "the backward pass has kernels for d=64 and d=128 only, not d=%d", d);
   if ((st = check_heads(Hq, Hkv)) != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||

@@ -9,9 +9,9 @@
 // The split kernel is a streaming read of K and V rows: arithmetic intensity is about
 // one flop per byte, so it is bound by HBM, not by the matrix cores, and runs on the
 // vector ALUs.  One wave owns one chunk.  A cache row (d 16-bit values) is read by d/8
-// lanes with one 16-byte load each, so one wave-wide load covers consecutive rows in
-// one contiguous kilobyte; two iterations of four such loads of K and of V are in
-// flight per lane.  The wave's row groups are combined with cross-lane exchanges,
+// lanes with one 16-byte load each (d = 96: a group of 16 lanes, of which 12 load), so
+// one wave-wide load covers consecutive rows of one contiguous stretch; two iterations
+// of four such loads of K and of V are in flight per lane.  The wave's row groups are combined with cross-lane exchanges,
 // so the kernel needs neither LDS nor barriers and many chunk-waves share a CU.
 // Scores are kept in the base-2 domain (c = scale*log2(e)).
 //
@@ -78,8 +78,9 @@ template <int DT, int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 2))) void decode_split_kernel(
     DecodeParams p) {
   using namespace decode_cfg;
-  constexpr int LPR = D / 8;      // lanes per cache row
-  constexpr int RPW = 64 / LPR;   // rows per wave-wide load
+  constexpr int CH = D / 8;                  // 16-byte chunks of a row
+  constexpr int LPR = CH == 12 ? 16 : CH;    // lanes per cache row (a power of two)
+  constexpr int RPW = 64 / LPR;              // rows per wave-wide load
   constexpr int RITER = RPW * kUnroll;
 
   const int s = blockIdx.x, b = blockIdx.z;
@@ -97,13 +98,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
 
   const int seg = lane % LPR;   // which 8 elements of d
   const int rsub = lane / LPR;  // row within one wave-wide load
+  const bool seg_ok = seg < CH; // lanes past the row's data (d = 96) load zeros and store nothing
   const size_t kvpair = (size_t)b * p.Hkv + kvh;
   const uint16_t* kg = p.k + kvpair * p.max_len * D + seg * 8;
   const uint16_t* vg = p.v + kvpair * p.max_len * D + seg * 8;
 
   u32x4 qp[G];  // this lane's 8 elements of each head's query row, packed as stored
 #pragma unroll
-  for (int j = 0; j < G; ++j) qp[j] = *(const u32x4*)(p.q + (pair0 + j) * D + seg * 8);
+  for (int j = 0; j < G; ++j) qp[j] = seg_ok ? *(const u32x4*)(p.q + (pair0 + j) * D + seg * 8) : (u32x4){0, 0, 0, 0};
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
       const int row = base + u * RPW + rsub;
       kr[u] = (u32x4){0, 0, 0, 0};
       vr[u] = (u32x4){0, 0, 0, 0};
-      if (row < r1) {
+      if (row < r1 && seg_ok) {
         kr[u] = *(const u32x4*)(kg + (size_t)row * D);
         vr[u] = *(const u32x4*)(vg + (size_t)row * D);
       }
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
       combine(m[j], l[j], acc[j], m2, l2, acc2);
     }
   }
-  if (rsub == 0) {
+  if (rsub == 0 && seg_ok) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const size_t pidx = (pair0 + j) * p.n_split + s;
@@ -214,7 +216,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel(DecodeParams p) {
   using namespace decode_cfg;
   constexpr int NG = kMergeThreads / 64;
-  constexpr int DPT = D / 64;  // d elements per thread
+  constexpr int DPT = (D + 63) / 64;  // d elements per thread (the last pass may be partial)
   constexpr int NBAT = 8;      // splits per group per round
   __shared__ float sm_M[NG];
   __shared__ float sm_den[NG];
@@ -243,7 +245,8 @@ __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel
       if (s < nv) {
         mlv[i] = *(const float2*)(ml + 2 * s);
 #pragma unroll
-        for (int x = 0; x < DPT; ++x) av[i][x] = ac[(size_t)s * D + x * 64 + lane];
+        for (int x = 0; x < DPT; ++x)
+          if (x * 64 + lane < D) av[i][x] = ac[(size_t)s * D + x * 64 + lane];
       }
     }
     float Mb = M;
@@ -271,7 +274,8 @@ __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel
   const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mall);
   if (lane == 0) sm_den[g] = den * sc;
 #pragma unroll
-  for (int x = 0; x < DPT; ++x) sm_num[g][x * 64 + lane] = num[x] * sc;
+  for (int x = 0; x < DPT; ++x)
+    if (x * 64 + lane < D) sm_num[g][x * 64 + lane] = num[x] * sc;
   __syncthreads();
   if (g == 0) {
     float dn = 0.f;
@@ -282,11 +286,11 @@ __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel
       const int d = x * 64 + lane;
       float nm = 0.f;
 #pragma unroll
-      for (int i = 0; i < NG; ++i) nm += sm_num[i][d];
+      for (int i = 0; i < NG; ++i) nm += d < D ? sm_num[i][d] : 0.f;
       const float o = dn > 0.f ? nm / dn : 0.f;  // a length of 0 leaves every chunk empty
       // Pair up neighbouring lanes so each even lane stores one dword.
       const float o_next = __shfl_down(o, 1);
-      if ((lane & 1) == 0) *(uint32_t*)(p.o + pair * D + d) = pack2<DT>(o, o_next);
+      if ((lane & 1) == 0 && d < D) *(uint32_t*)(p.o + pair * D + d) = pack2<DT>(o, o_next);
     }
   }
 }
@@ -342,10 +346,15 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
   p.n_split = n_split;
   p.c = scale * kLog2e;
   const int G = decode_heads_per_wave(H, Hkv);
-  if (dt == DT_F16 && d == 64) return launch_decode_g<DT_F16, 64>(p, G, st);
-  if (dt == DT_F16 && d == 128) return launch_decode_g<DT_F16, 128>(p, G, st);
-  if (dt == DT_BF16 && d == 64) return launch_decode_g<DT_BF16, 64>(p, G, st);
-  if (dt == DT_BF16 && d == 128) return launch_decode_g<DT_BF16, 128>(p, G, st);
+#define ATTN_DEC(D_)                                                          \
+  if (dt == DT_F16 && d == D_) return launch_decode_g<DT_F16, D_>(p, G, st); \
+  if (dt == DT_BF16 && d == D_) return launch_decode_g<DT_BF16, D_>(p, G, st);
+  ATTN_DEC(64)
+  ATTN_DEC(128)
+  ATTN_DEC(32)
+  ATTN_DEC(96)
+  ATTN_DEC(256)
+#undef ATTN_DEC
   return hipErrorInvalidValue;
 }
 

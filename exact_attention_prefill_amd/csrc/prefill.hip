@@ -58,19 +58,35 @@ struct PrefillParams {
   float* lse;     // optional [B][H][N] row log-sum-exp (natural log), or null
 };
 
+// LDS row pitch of a K/V tile: rows of d = 32 and d = 96 are padded to the pitch of
+// d = 64 and d = 128, so every head size uses one of two swizzle families.
+template <int D>
+constexpr int lds_row_bytes() {
+  return D == 32 ? 128 : D == 96 ? 256 : 2 * D;
+}
+
+// Two waves per SIMD need <= 256 registers a wave: QB = 1 up to d = 128.
+template <int D, int QB>
+constexpr int prefill_waves_per_simd() {
+  return (QB == 1 && D <= 128) ? 2 : 1;
+}
+
 // NW waves per workgroup, each owning QB blocks of 32 query rows.  QB = 1: two waves
-// share each SIMD (<= 256 registers).  QB = 2: the two row blocks share every K and V
+// share each SIMD (<= 256 registers, up to d = 128).  QB = 2: the two row blocks share every K and V
 // operand read, halving LDS traffic per MFMA; a wave then needs ~350 registers, so
 // one wave runs per SIMD with the MFMA accumulators in AGPRs.
 template <int DT, int D, bool CAUSAL, int NW, int QB>
-__global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
   using namespace prefill_cfg;
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
   constexpr int QW = 32 * QB;                      // query rows per wave
   constexpr int BM = QW * NW;                      // query rows per workgroup
-  constexpr int RB = D * 2;                        // bytes per K/V row
+  constexpr int RBG = D * 2;                       // bytes per K/V row in memory
+  constexpr int RB = lds_row_bytes<D>();           // bytes per K/V row in LDS
+  constexpr int CH = D / 8;                        // 16-byte chunks of a row that hold data
+  constexpr bool W256 = RB % 256 == 0;             // swizzle family (rows of 256 or 512 bytes)
   constexpr int KS = D / 16;                       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;                       // 32-wide output blocks along d
   constexpr int TILE_BYTES = BN * RB;              // one K (or V) tile
@@ -133,22 +149,27 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   // by XOR with a per-row key so that both operand reads are free of bank conflicts
   // (64 banks of 4 bytes; a wave's read is served 256 bytes per cycle, in halves of 32
   // lanes for the transpose reads).  K reads (one chunk of each of 32 consecutive
-  // rows; 16 rows per pass): key row & 15 (d=128) or (row>>1) & 7 (d=64).  V^T
-  // transpose reads (per 32-lane half: 4 rows x 4 consecutive chunks): the four rows
-  // must land on four disjoint 64-byte bank groups, key 4*(row & 3) (d=128, rows of
-  // 256 B) or 4*((row>>1) & 1) (d=64, rows of 128 B, odd rows already offset by 128 B).
-  auto kkey = [](int row) __attribute__((always_inline)) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
-  auto vkey = [](int row) __attribute__((always_inline)) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
+  // rows; 16 rows per pass): key row & 15 (rows of 256 or 512 B, a multiple of the
+  // bank width) or (row>>1) & 7 (rows of 128 B).  V^T transpose reads (per 32-lane
+  // half: 4 rows x 4 consecutive chunks): the four rows must land on four disjoint
+  // 64-byte bank groups, key 4*(row & 3) (rows of 256 or 512 B) or 4*((row>>1) & 1)
+  // (rows of 128 B, odd rows already offset by 128 B).  The keys stay below the
+  // row's chunk count, so a swizzled chunk stays in its row.
+  auto kkey = [](int row) __attribute__((always_inline)) { return W256 ? (row & 15) : ((row >> 1) & 7); };
+  auto vkey = [](int row) __attribute__((always_inline)) { return W256 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
   // LDS-direct load r of this wave fills LDS chunk ci = (wave*NLD + r)*64 + lane, i.e.
   // row ci / (RB/16) and physical slot ci % (RB/16), which holds logical chunk
-  // slot ^ key(row): fetch that chunk from memory.
+  // slot ^ key(row): fetch that chunk from memory.  Padded rows (d = 32, 96) have
+  // logical chunks past the data; those slots are never read and take a copy of a
+  // chunk of the same row.
+  auto src_chunk = [](int c) __attribute__((always_inline)) { return c >= CH ? c - CH : c; };
   uint32_t ldk_off[NLD], ldv_off[NLD];
 #pragma unroll
   for (int r = 0; r < NLD; ++r) {
     const int ci = (wave * NLD + r) * 64 + lane;
     const int row = ci / (RB / 16), sl = ci % (RB / 16);
-    ldk_off[r] = row * RB + ((sl ^ kkey(row)) << 4);
-    ldv_off[r] = row * RB + ((sl ^ vkey(row)) << 4);
+    ldk_off[r] = row * RBG + (src_chunk(sl ^ kkey(row)) << 4);
+    ldv_off[r] = row * RBG + (src_chunk(sl ^ vkey(row)) << 4);
   }
   // K operand (A of S^T): row 32kb + l32 (key(row) does not depend on kb), logical
   // chunk 2ks + half.
@@ -204,10 +225,10 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   auto load_tile = [&](const char* src_base, const uint32_t (&offs)[NLD], int t, char* dst) __attribute__((always_inline)) {
     const int k0 = t * BN;
     const int rows_left = N - k0;
-    const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RB;
+    const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RBG;
     // Buffer descriptor: base address, stride 0, nrec bytes in range (rows past the
     // end read nothing), raw dword format.
-    const u32x4 r = buffer_rsrc(src_base + (size_t)k0 * RB, nrec);
+    const u32x4 r = buffer_rsrc(src_base + (size_t)k0 * RBG, nrec);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst) + wave * NLD * 1024);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) lds_dma16(r, offs[i], l0 + i * 1024);
@@ -290,8 +311,10 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   // pnext receives P_{u+1}.  kb_ holds K of unit u+2 and vb_ V of unit u, each in half h.
   // Near the end of a wave's range S_{u+2} may score keys it never uses: such a unit
   // is fully masked when it is consumed, so m and l do not move and P is zero.
-  // Eight issue slots per iteration.  d = 128: slot i issues score MFMA i and P*V MFMA
-  // i (s = i/4, db = i%4).  d = 64 (4 + 4 MFMAs): even slots score, odd slots P*V.
+  // Eight issue slots per iteration (one per dword of P).  Score MFMA a goes to slot
+  // 8a / KS and P*V MFMA b to slot 8b / NP plus an offset that puts it between two
+  // score slots when there are fewer than eight: d = 128 issues one of each per slot,
+  // d = 64 alternates, d = 256 issues two of each per slot.
   // Each K or V operand read feeds the MFMAs of all QB row blocks.
   // Operands are read PF MFMAs ahead into a ring of PF + 1 registers that spans the
   // tile: operand a of the tile's unit h sits in slot (h*KS + a) mod (PF + 1) (K) or
@@ -301,8 +324,9 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
   constexpr int NP = 2 * DB;  // P*V MFMAs per unit and row block
   constexpr int PF = 2;       // operand prefetch distance (MFMAs of the same kind)
   constexpr int R = PF + 1;   // operand ring size
-  auto s_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 0 ? i >> 1 : -1); };
-  auto p_at = [](int i) __attribute__((always_inline)) { return D == 128 ? i : ((i & 1) == 1 ? i >> 1 : -1); };
+  constexpr int P_OFF = NP >= 8 ? 0 : (4 / NP > 1 ? 4 / NP : 1);
+  auto s_slot = [](int a) __attribute__((always_inline)) { return 8 * a / KS; };
+  auto p_slot = [](int b) __attribute__((always_inline)) { return 8 * b / NP + P_OFF; };
   auto iterate = [&](int u, f32x16 (&scur)[QB], f32x16 (&snext)[QB], const u32x4 (&pcur)[QB][2],
                      u32x4 (&pnext)[QB][2], const char* kb_, const char* vb_, int h, u32x4 (&kf)[R],
                      u32x4 (&vf)[R]) __attribute__((always_inline)) {
@@ -318,15 +342,18 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 2 : 1) void prefill_kernel(Prefi
     for (int cb = 0; cb < QB; ++cb) p_arg(scur[cb], neg_m[cb], 0, xa[cb]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int a = s_at(i), b = p_at(i);
-      if (a >= 0) {
+#pragma unroll
+      for (int a = 0; a < KS; ++a) {
+        if (s_slot(a) != i) continue;
         if (a + PF < KS) kf[(kg + a + PF) % R] = kread(kb_, h, a + PF);
         else if (h == 0) kf[(kg + a + PF) % R] = kread(kb_, 1, a + PF - KS);
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb)  // the first MFMA of a chain takes a literal zero addend
           snext[cb] = mfma32x32x16<DT>(kf[(kg + a) % R], qf[cb][a], a == 0 ? (f32x16){} : snext[cb]);
       }
-      if (b >= 0) {
+#pragma unroll
+      for (int b = 0; b < NP; ++b) {
+        if (p_slot(b) != i) continue;
         if (b + PF < NP) vf[(vg + b + PF) % R] = vread(vb_, h, (b + PF) / DB, (b + PF) % DB);
         else if (h == 0) vf[(vg + b + PF) % R] = vread(vb_, 1, (b + PF - NP) / DB, (b + PF - NP) % DB);
 #pragma unroll
@@ -471,9 +498,16 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   // at least four such workgroups, and small grids keep the finer four-wave blocks.
   // The 64-row form (QB = 2) halves LDS operand reads per MFMA but, at one wave per
   // SIMD, measured 5-8% slower, so it is not selected.
-  const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-  if (blocks8 >= 4LL * num_cus) return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
-  return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
+  // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
+  // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
+  // workgroup per CU.
+  if constexpr (D > 128) {
+    return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
+  } else {
+    const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
+    if (blocks8 >= 4LL * num_cus) return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
+    return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
+  }
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
@@ -497,14 +531,17 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   p.qand = scale == 0.f ? 0u : 0xffffffffu;
 #define ATTN_PF(DT_, D_, C_) \
   if (dt == DT_ && d == D_ && causal == C_) return launch_prefill_w<DT_, D_, C_>(p, num_cus, s);
-  ATTN_PF(DT_F16, 64, false)
-  ATTN_PF(DT_F16, 64, true)
-  ATTN_PF(DT_F16, 128, false)
-  ATTN_PF(DT_F16, 128, true)
-  ATTN_PF(DT_BF16, 64, false)
-  ATTN_PF(DT_BF16, 64, true)
-  ATTN_PF(DT_BF16, 128, false)
-  ATTN_PF(DT_BF16, 128, true)
+#define ATTN_PF_D(D_)         \
+  ATTN_PF(DT_F16, D_, false)  \
+  ATTN_PF(DT_F16, D_, true)   \
+  ATTN_PF(DT_BF16, D_, false) \
+  ATTN_PF(DT_BF16, D_, true)
+  ATTN_PF_D(64)
+  ATTN_PF_D(128)
+  ATTN_PF_D(32)
+  ATTN_PF_D(96)
+  ATTN_PF_D(256)
+#undef ATTN_PF_D
 #undef ATTN_PF
   return hipErrorInvalidValue;
 }

@@ -53,7 +53,8 @@ typedef enum {
 /* Prefill (page 3, "What can it do": prompt phase; "Installation": prefill(q, k, v,
  * causal, scale)).
  *   q, k, v : [B][H][N][d] inputs;  out : [B][H][N][d] output, must not alias an input.
- *   B, H, N >= 1;  d in {64, 128};  dtype ATTN_F16 or ATTN_BF16;  causal in {0, 1}
+ *   B, H, N >= 1;  d in {32, 64, 96, 128, 256} (page 3, "Future work": head sizes
+ *   beyond its 64);  dtype ATTN_F16 or ATTN_BF16;  causal in {0, 1}
  *   (1: key j is visible to query row i iff j <= i).
  * Allocates nothing.  Returns ATTN_OK or a negative attn_status. */
 int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -157,7 +158,8 @@ int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int
  *   workspace : DEVICE buffer of at least attn_backward_workspace_bytes(B, Hq, N) bytes
  *   (16-byte aligned; contents on entry do not matter), or NULL with ws_bytes 0 for a
  *   stream-ordered allocation.
- * Same dtype, layout, validation and asynchrony rules as attn_prefill.  Deterministic:
+ * Same dtype, layout, validation and asynchrony rules as attn_prefill, except that d
+ * is 64 or 128 (ATTN_ERR_UNSUPPORTED otherwise).  Deterministic:
  * no atomics, every output element written by one wave. */
 int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int dtype, int causal,

@@ -46,8 +46,10 @@ def _prefill(**kw):
         (dict(B=0), ea.ATTN_ERR_INVALID_ARG),
         (dict(H=-1), ea.ATTN_ERR_INVALID_ARG),
         (dict(N=0), ea.ATTN_ERR_INVALID_ARG),
-        (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
-        (dict(d=32), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=48), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=512), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=16), ea.ATTN_ERR_UNSUPPORTED),
         (dict(dt=2), ea.ATTN_ERR_INVALID_ARG),
         (dict(causal=2), ea.ATTN_ERR_INVALID_ARG),
         (dict(scale=float("nan")), ea.ATTN_ERR_INVALID_ARG),
@@ -77,7 +79,8 @@ def _decode_ex(**kw):
     [
         (dict(B=0), ea.ATTN_ERR_INVALID_ARG),
         (dict(max_len=0), ea.ATTN_ERR_INVALID_ARG),
-        (dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=192), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=160), ea.ATTN_ERR_UNSUPPORTED),
         (dict(lens=None), ea.ATTN_ERR_INVALID_ARG),
         (dict(lens=P[4] + 2), ea.ATTN_ERR_ALIGNMENT),
         (dict(chunk=16), ea.ATTN_ERR_INVALID_ARG),
@@ -230,7 +233,10 @@ def _backward(**kw):
     "kw,status",
     [
         (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG),
-        (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),  # a forward head size without backward kernels
+        (dict(d=32), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), ea.ATTN_ERR_UNSUPPORTED),
         (dict(lse=None), ea.ATTN_ERR_INVALID_ARG),
         (dict(lse=P[5] + 2), ea.ATTN_ERR_ALIGNMENT),
         (dict(dq=P[0]), ea.ATTN_ERR_INVALID_ARG),  # gradient aliases q

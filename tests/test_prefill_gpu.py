@@ -182,7 +182,7 @@ def test_last_causal_row_matches_full():
 
 
 def test_python_errors():
-    q = torch.zeros(1, 1, 8, 96, dtype=torch.float16, device=DEV)
+    q = torch.zeros(1, 1, 8, 80, dtype=torch.float16, device=DEV)
     with pytest.raises(ValueError):
         ea.prefill(q, q.clone(), q.clone())
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
