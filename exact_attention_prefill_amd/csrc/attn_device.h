@@ -78,6 +78,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---- LDS staging and cross-lane helpers shared by the attention kernels ----
 
+// LDS row pitch of a staged K/V tile: rows of d = 32 and d = 96 are padded to the
+// pitch of d = 64 and d = 128, so every head size uses one of two swizzle families
+// (rows of 128 bytes, or a multiple of 256).
+template <int D>
+constexpr int lds_row_bytes() {
+  return D == 32 ? 128 : D == 96 ? 256 : 2 * D;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt at their "no wait" maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... until every LDS operation of this wave has completed (vmcnt and expcnt not waited).
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 

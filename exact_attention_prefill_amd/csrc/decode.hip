@@ -27,6 +27,7 @@ namespace attn {
 namespace decode_cfg {
 constexpr int kUnroll = 4;          // row loads of K (and of V) per lane per buffer (two buffers)
 constexpr int kMergeThreads = 256;  // merge workgroup: 4 split groups x 64
+constexpr int kMfmaMinGroup = 3;    // smallest group of query heads decoded on the matrix cores
 }  // namespace decode_cfg
 
 struct DecodeParams {
@@ -207,6 +208,190 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
   }
 }
 
+// Grouped heads on the matrix cores.  One wave per (split, K/V head, batch) scores
+// all g query heads of the group at once: they are the columns of one 32-wide MFMA
+// tile (g <= 32; columns past g hold zeros), exactly as a block of query rows is in
+// the prefill.  The chunk's K and V rows stream through LDS in 32-row tiles
+// (LDS-direct loads, two stages, the prefill's swizzles):
+//   S^T = K Q^T (one query head per lane column, 16 keys per lane),
+//   per head: m, l and the rescale of O as in the online softmax,
+//   O^T += V^T P^T with V^T from LDS transpose reads and P rounded to 16 bits.
+// The partials (m, l, acc) have the split kernel's layout, per query head.  Per byte
+// of cache read this takes a few VALU instructions however many heads the group has,
+// where the VALU form spends them once per head.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int RBG = 2 * D;                 // bytes per cache row in memory
+  constexpr int RB = lds_row_bytes<D>();     // bytes per row in LDS
+  constexpr int CH = D / 8;                  // 16-byte chunks of a row that hold data
+  constexpr bool W256 = RB % 256 == 0;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int UK = 32;                     // keys per tile (one MFMA block)
+  constexpr int TILE = UK * RB;
+  constexpr int NLD = TILE / 1024;           // 1 KiB LDS-direct loads per tile and operand
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
+
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+  const int g = p.g;
+  // Uniform values the buffer descriptors are built from are pinned to SGPRs.
+  const int L = __builtin_amdgcn_readfirstlane(clamp_len(p.seq_lens[b], p.max_len));
+  const int r0 = s * p.chunk;
+  const size_t pair0 = (size_t)b * p.H + (size_t)kvh * g;  // the group's first query head
+  if (r0 >= L) {  // empty chunk: mark it so the merge needs no lengths
+    if (lane < g) *(float2*)(p.ws_ml + ((pair0 + lane) * p.n_split + s) * 2) = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const int r1 = min(L, r0 + p.chunk);
+  const int nu = (r1 - r0 + UK - 1) / UK;
+  const size_t kvpair = (size_t)b * p.Hkv + kvh;
+  const char* kbase = (const char*)(p.k + kvpair * p.max_len * D);
+  const char* vbase = (const char*)(p.v + kvpair * p.max_len * D);
+  const bool col_ok = l32 < g;
+
+  // Q^T as the B operand: lane holds q[head l32][16ks + 8half + 0..7].
+  u32x4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = col_ok ? *(const u32x4*)(p.q + (pair0 + l32) * D + 16 * ks + 8 * half) : (u32x4){0, 0, 0, 0};
+
+  auto kkey = [](int row) __attribute__((always_inline)) { return W256 ? (row & 15) : ((row >> 1) & 7); };
+  auto vkey = [](int row) __attribute__((always_inline)) { return W256 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
+  auto src_chunk = [](int c) __attribute__((always_inline)) { return c >= CH ? c - CH : c; };
+  uint32_t ldk_off[NLD], ldv_off[NLD];
+#pragma unroll
+  for (int r = 0; r < NLD; ++r) {
+    const int ci = r * 64 + lane;
+    const int row = ci / (RB / 16), sl = ci % (RB / 16);
+    ldk_off[r] = row * RBG + (src_chunk(sl ^ kkey(row)) << 4);
+    ldv_off[r] = row * RBG + (src_chunk(sl ^ vkey(row)) << 4);
+  }
+  uint32_t k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * RB + (((2 * ks + half) ^ kkey(l32)) << 4);
+  uint32_t v_off[DB];
+  {
+    const int r = lane & 15, gg = (lane >> 4) & 1;
+    const int rowlo = 4 * half + (r >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
+      v_off[db] = rowlo * RB + ((chunk ^ vkey(rowlo)) << 4) + 8 * (r & 1);
+    }
+  }
+
+  if ((r1 - r0) % UK != 0) {
+    // The last tile is partial and its missing rows are never written: start from
+    // zeros so no uninitialised LDS bits reach the MFMA (masked p is exactly 0).
+    for (int i = lane; i < TILE / 16; i += 64) {
+      ((u32x4*)kbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)kbuf1)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf0)[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)vbuf1)[i] = (u32x4){0, 0, 0, 0};
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+
+  auto load_tile = [&](int u, char* kb, char* vb) __attribute__((always_inline)) {
+    const int row0 = r0 + u * UK;
+    const int left = r1 - row0;
+    const uint32_t nrec = (uint32_t)(left < UK ? left : UK) * RBG;
+    u32x4 rk = buffer_rsrc(kbase + (size_t)row0 * RBG, nrec);
+    u32x4 rv = buffer_rsrc(vbase + (size_t)row0 * RBG, nrec);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // uniform: keep the descriptors in SGPRs
+      rk[w] = __builtin_amdgcn_readfirstlane(rk[w]);
+      rv[w] = __builtin_amdgcn_readfirstlane(rv[w]);
+    }
+    const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr_of(kb));
+    const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr_of(vb));
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rk, ldk_off[i], lk + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rv, ldv_off[i], lv + i * 1024);
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Unit u from the tile in (kb, vb); `next` says whether the following tile's loads
+  // were issued after this one's (then they may stay in flight).
+  auto unit = [&](int u, const char* kb, const char* vb, bool next) __attribute__((always_inline)) {
+    if (next) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NLD));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    f32x16 st = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) st = mfma32x32x16<DT>(lds_read_b128((const uint16_t*)kb, k_off[ks]), qf[ks], st);
+    const int key0 = r0 + u * UK + 4 * half;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + 8 * (i >> 2) + (i & 3);
+      st[i] = key < r1 ? st[i] * p.c : -INFINITY;
+      mx = fmaxf(mx, st[i]);
+    }
+    // Key r0 + 32u is in range, so every column's max is finite.
+    const float m_new = fmaxf(m_run, xhalf_max(mx));
+    const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf gives 0
+    m_run = m_new;
+    u32x4 pf[2];
+    float lu = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t t = pack2<DT>(fast_exp2(st[2 * w] - m_new), fast_exp2(st[2 * w + 1] - m_new));
+      pf[w >> 2][w & 3] = t;
+      lu = add_pair<DT>(t, lu);  // l sums the rounded weights that enter the MFMA
+    }
+    l_run = l_run * alpha + lu;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t off = v_off[db] + 16 * si * RB;
+        const u32x2 lo = lds_read_tr((const uint16_t*)vb, off);
+        const u32x2 hi = lds_read_tr((const uint16_t*)vb, off + 8 * RB);
+        oacc[db] = mfma32x32x16<DT>((u32x4){lo[0], lo[1], hi[0], hi[1]}, pf[si], oacc[db]);
+      }
+    // Every read of this tile has returned before the buffers take another tile.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  };
+
+  load_tile(0, kbuf0, vbuf0);
+  if (nu > 1) load_tile(1, kbuf1, vbuf1);
+  for (int u = 0; u < nu; u += 2) {
+    unit(u, kbuf0, vbuf0, u + 1 < nu);
+    if (u + 2 < nu) load_tile(u + 2, kbuf0, vbuf0);
+    if (u + 1 < nu) {
+      unit(u + 1, kbuf1, vbuf1, u + 2 < nu);
+      if (u + 3 < nu) load_tile(u + 3, kbuf1, vbuf1);
+    }
+  }
+
+  // Column l32 is query head pair0 + l32; its keys are split over the two lane
+  // halves, its d rows too: acc row 32db + 8(i/4) + 4half + i%4.
+  const float l_tot = xhalf_sum(l_run);
+  if (col_ok) {
+    const size_t pidx = (pair0 + l32) * p.n_split + s;
+    float* out = p.ws_acc + pidx * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4*)(out + 32 * db + 8 * a + 4 * half) =
+            (f32x4){oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]};
+    if (half == 0) *(float2*)(p.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+  }
+#endif
+}
+
 // Exact merge: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the non-empty
 // splits (empty ones carry m = -inf); a length of 0 writes zeros.  Four groups of 64
 // threads take every fourth split, eight splits per round, each round's loads issued
@@ -305,7 +490,17 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
 }
 
 template <int DT, int D>
+static hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((decode_split_mfma_kernel<DT, D>), dim3(p.n_split, p.Hkv, p.B), dim3(64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(decode_cfg::kMergeThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
 static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) {
+  if (G == p.g && G >= decode_cfg::kMfmaMinGroup) return launch_decode_mfma<DT, D>(p, st);
   switch (G) {
     case 1: return launch_decode_t<DT, D, 1>(p, st);
     case 2: return launch_decode_t<DT, D, 2>(p, st);
@@ -321,6 +516,9 @@ static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) 
 
 int decode_heads_per_wave(int H, int Hkv) {
   const int g = H / Hkv;
+  // Groups of 3..32 query heads: one matrix-core wave serves the whole group (pairs
+  // of heads measured faster on the vector ALUs).
+  if (g >= decode_cfg::kMfmaMinGroup && g <= 32) return g;
   for (int G = 8; G > 1; --G)
     if (g % G == 0) return G;
   return 1;

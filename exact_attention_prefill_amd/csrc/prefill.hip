@@ -58,13 +58,6 @@ struct PrefillParams {
   float* lse;     // optional [B][H][N] row log-sum-exp (natural log), or null
 };
 
-// LDS row pitch of a K/V tile: rows of d = 32 and d = 96 are padded to the pitch of
-// d = 64 and d = 128, so every head size uses one of two swizzle families.
-template <int D>
-constexpr int lds_row_bytes() {
-  return D == 32 ? 128 : D == 96 ? 256 : 2 * D;
-}
-
 // Two waves per SIMD need <= 256 registers a wave: QB = 1 up to d = 128.
 template <int D, int QB>
 constexpr int prefill_waves_per_simd() {

@@ -136,9 +136,10 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, floa
  * chunk / workspace / ws_bytes as for attn_decode_ex (chunk 0: automatic, from
  * attn_decode_gqa_choose_split; workspace NULL with ws_bytes 0: stream-ordered
  * allocation).  The workspace holds partials per query head:
- * attn_decode_workspace_bytes(B, Hq, n_split, d).  Each split wave reads its K/V rows
- * once for up to 8 query heads of one group, so the cache is read once per group of
- * up to 8 heads rather than once per query head. */
+ * attn_decode_workspace_bytes(B, Hq, n_split, d).  Groups of 3 to 32 query heads per
+ * K/V head are scored together on the matrix cores, one split wave per K/V head, so the
+ * cache is read once per group; otherwise each split wave reads its K/V rows once for
+ * up to 8 query heads of one group. */
 int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                     int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
                     size_t ws_bytes, void* stream);
