@@ -25,6 +25,7 @@ ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGNMENT, ATTN_ERR_WORKSPA
 DECODE_ROW_GRANULE = 32
 DECODE_WGS_PER_CU = 8
 DECODE_MIN_CHUNK = 64
+DECODE_MFMA_LDS_BYTES = 163840
 
 # Every symbol include/attn.h declares.
 EXPORTS = (

@@ -18,6 +18,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
                          int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
                          hipStream_t st);
 int decode_heads_per_wave(int H, int Hkv);
+bool decode_uses_mfma(int H, int Hkv);
+int decode_mfma_waves_per_cu(int d);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
                            int d, int dt, int causal, float scale, hipStream_t s);
@@ -142,15 +144,10 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, floa
   return prefill_impl(q, k, v, out, lse, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
 }
 
-int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {
-  if (B < 1 || H < 1 || max_len < 1 || num_cus < 1)
-    return fail(ATTN_ERR_INVALID_ARG, "B, H, max_len and num_cus must be >= 1");
-  if (!head_dim_ok(d))
-    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
-  if (!chunk || !n_split) return fail(ATTN_ERR_INVALID_ARG, "chunk and n_split must be non-NULL host pointers");
+// The split for `pairs` wave columns (one wave per column and split) aiming at
+// `target` waves in all.
+static void choose_split_core(long long pairs, int max_len, long long target, int* chunk, int* n_split) {
   const long long T = ATTN_DECODE_ROW_GRANULE;
-  const long long pairs = (long long)B * H;
-  const long long target = (long long)ATTN_DECODE_WGS_PER_CU * num_cus;
   // Smallest chunk: ATTN_DECODE_MIN_CHUNK rows, or the whole (granule-rounded) cache
   // when it is shorter.
   const long long rounded_len = (max_len + T - 1) / T * T;
@@ -167,6 +164,15 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
   while (c - T >= cmin && pairs * ((max_len + c - 1) / c) < target) c -= T;
   *chunk = (int)c;
   *n_split = (int)((max_len + c - 1) / c);
+}
+
+int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int* chunk, int* n_split) {
+  if (B < 1 || H < 1 || max_len < 1 || num_cus < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "B, H, max_len and num_cus must be >= 1");
+  if (!head_dim_ok(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
+  if (!chunk || !n_split) return fail(ATTN_ERR_INVALID_ARG, "chunk and n_split must be non-NULL host pointers");
+  choose_split_core((long long)B * H, max_len, (long long)ATTN_DECODE_WGS_PER_CU * num_cus, chunk, n_split);
   return ok();
 }
 
@@ -222,8 +228,17 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
 int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split) {
   if (Hq < 1 || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
     return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must divide the query head count Hq=%d", Hkv, Hq);
+  if (B < 1 || max_len < 1 || num_cus < 1) return fail(ATTN_ERR_INVALID_ARG, "B, max_len and num_cus must be >= 1");
+  if (!head_dim_ok(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
+  if (!chunk || !n_split) return fail(ATTN_ERR_INVALID_ARG, "chunk and n_split must be non-NULL host pointers");
   // One wave serves decode_heads_per_wave query heads: that many fewer waves per split.
-  return attn_decode_choose_split(B, Hq / attn::decode_heads_per_wave(Hq, Hkv), max_len, d, num_cus, chunk, n_split);
+  const long long cols = (long long)B * (Hq / attn::decode_heads_per_wave(Hq, Hkv));
+  // The matrix-core form holds LDS tiles, so fewer of its waves fit on a CU: aim at
+  // one resident round of them rather than at the vector form's target.
+  const int per_cu = attn::decode_uses_mfma(Hq, Hkv) ? attn::decode_mfma_waves_per_cu(d) : ATTN_DECODE_WGS_PER_CU;
+  choose_split_core(cols, max_len, (long long)per_cu * num_cus, chunk, n_split);
+  return ok();
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d) {

@@ -20,6 +20,7 @@
 //   ml [(pair*n_split + s)*2 + 0, 1]      m = max_t c s_t, l = sum_t 2^(c s_t - m)
 // where acc is the first B*H*n_split*d floats and ml follows it.  A chunk at or past
 // the sequence's length writes only (m, l) = (-inf, 0); its acc is never read.
+#include "attn.h"
 #include "attn_device.h"
 
 namespace attn {
@@ -44,6 +45,15 @@ struct DecodeParams {
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
+
+// Split handled by this workgroup of a (n_split, columns...) grid.  Workgroups are
+// dealt to the 8 XCDs round-robin by linear id, so with a split count that is a
+// multiple of 8 split s of every column would land on XCD s mod 8; the sequences'
+// non-empty splits are prefixes, which would load the low XCDs more.  Skewing the
+// split by the column index starts each column on another XCD.
+__device__ __forceinline__ int skewed_split(int n_split) {
+  return (int)((blockIdx.x + blockIdx.y + (unsigned)blockIdx.z * gridDim.y) % (unsigned)n_split);
+}
 
 // Dot product of two packed pairs of 16-bit values, accumulated in fp32.
 template <int DT>
@@ -84,7 +94,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
   constexpr int RPW = 64 / LPR;              // rows per wave-wide load
   constexpr int RITER = RPW * kUnroll;
 
-  const int s = blockIdx.x, b = blockIdx.z;
+  const int b = blockIdx.z;
+  const int s = skewed_split(p.n_split);
   const int h0 = blockIdx.y * G;  // first query head of this wave
   const int kvh = h0 / p.g;       // the K/V head all G of them read
   const int L = clamp_len(p.seq_lens[b], p.max_len);
@@ -235,7 +246,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
 
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int s = skewed_split(p.n_split);
   const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
   const int g = p.g;
   // Uniform values the buffer descriptors are built from are pinned to SGPRs.
@@ -489,6 +501,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool decode_uses_mfma(int H, int Hkv);
+
 template <int DT, int D>
 static hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_mfma_kernel<DT, D>), dim3(p.n_split, p.Hkv, p.B), dim3(64), 0, st, p);
@@ -500,7 +514,7 @@ static hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t st) {
 
 template <int DT, int D>
 static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) {
-  if (G == p.g && G >= decode_cfg::kMfmaMinGroup) return launch_decode_mfma<DT, D>(p, st);
+  if (decode_uses_mfma(p.H, p.Hkv)) return launch_decode_mfma<DT, D>(p, st);
   switch (G) {
     case 1: return launch_decode_t<DT, D, 1>(p, st);
     case 2: return launch_decode_t<DT, D, 2>(p, st);
@@ -514,11 +528,23 @@ static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) 
   }
 }
 
-int decode_heads_per_wave(int H, int Hkv) {
-  const int g = H / Hkv;
+bool decode_uses_mfma(int H, int Hkv) {
   // Groups of 3..32 query heads: one matrix-core wave serves the whole group (pairs
   // of heads measured faster on the vector ALUs).
-  if (g >= decode_cfg::kMfmaMinGroup && g <= 32) return g;
+  const int g = H / Hkv;
+  return g >= decode_cfg::kMfmaMinGroup && g <= 32;
+}
+
+// Resident waves per CU of the matrix-core split kernel: its two K and two V tiles of
+// 32 rows take the CU's LDS first (registers allow at least as many).
+int decode_mfma_waves_per_cu(int d) {
+  const int pitch = d == 32 ? 128 : d == 96 ? 256 : 2 * d;
+  return ATTN_DECODE_MFMA_LDS_BYTES / (4 * 32 * pitch);
+}
+
+int decode_heads_per_wave(int H, int Hkv) {
+  const int g = H / Hkv;
+  if (decode_uses_mfma(H, Hkv)) return g;
   for (int G = 8; G > 1; --G)
     if (g % G == 0) return G;
   return 1;

@@ -95,6 +95,9 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
 /* Split chunks (one wave each) per compute unit that the automatic decode split aims for. */
 #define ATTN_DECODE_WGS_PER_CU 8
 
+/* LDS per compute unit that sizes the matrix-core decode split (160 KiB on gfx950). */
+#define ATTN_DECODE_MFMA_LDS_BYTES 163840
+
 /* Smallest chunk the automatic decode split picks (a multiple of the granule): below it
  * a wave's fixed work (query load, cross-lane combine, partial store) outweighs the
  * parallelism it adds.  Explicit chunks in attn_decode_ex may still be one granule. */
@@ -145,6 +148,13 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, con
                     size_t ws_bytes, void* stream);
 
 /* Host-only: the automatic split of attn_decode_gqa (writes HOST *chunk, *n_split).
+ * The rule of attn_decode_choose_split over the split waves' columns:
+ *   - groups of 3 to 32 query heads (matrix cores): B*Hkv columns, aiming at
+ *     ATTN_DECODE_MFMA_LDS_BYTES / (4 * 32 * pitch) waves per compute unit, the number
+ *     whose LDS tiles fit on one (pitch: 128 bytes for d = 32 and 64, 256 for d = 96
+ *     and 128, 512 for d = 256: 10, 5 and 2 waves);
+ *   - otherwise: B*Hq/G columns for G query heads per wave, aiming at
+ *     ATTN_DECODE_WGS_PER_CU waves per compute unit.
  * With Hkv == Hq it equals attn_decode_choose_split.  No HIP call. */
 int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split);
 

@@ -67,3 +67,45 @@ def test_binding_constants_match_header():
     assert int(defs["ATTN_DECODE_ROW_GRANULE"]) == ea.DECODE_ROW_GRANULE
     assert int(defs["ATTN_DECODE_WGS_PER_CU"]) == ea.DECODE_WGS_PER_CU
     assert int(defs["ATTN_DECODE_MIN_CHUNK"]) == ea.DECODE_MIN_CHUNK
+    assert int(defs["ATTN_DECODE_MFMA_LDS_BYTES"]) == ea.DECODE_MFMA_LDS_BYTES
+
+
+def split_rule(cols, max_len, target):
+    """The documented rule, written out: n = ceil(target / cols) clamped to what the
+    smallest chunk allows, chunk = ceil(max_len / n) rounded up to the granule (at least
+    the smallest chunk), then shrunk one granule at a time while the split count is
+    short of the target."""
+    cmin = min_chunk(max_len)
+    n = max(1, -(-target // cols))
+    n = min(n, -(-max_len // cmin))
+    c = max(cmin, -(-(-(-max_len // n)) // G) * G)
+    while c - G >= cmin and cols * (-(-max_len // c)) < target:
+        c -= G
+    return c, -(-max_len // c)
+
+
+@pytest.mark.parametrize("B,H,max_len,cus", list(itertools.product([1, 8, 64], [1, 12, 32], [100, 4096, 65536], [82, 256])))
+def test_rule_matches_library(B, H, max_len, cus):
+    assert ea.decode_choose_split(B, H, max_len, 64, cus) == split_rule(B * H, max_len, WGS_PER_CU * cus)
+
+
+def mfma_waves_per_cu(d):
+    pitch = {32: 128, 64: 128, 96: 256, 128: 256, 256: 512}[d]
+    return ea.DECODE_MFMA_LDS_BYTES // (4 * 32 * pitch)
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("B,Hq,Hkv", [(8, 32, 8), (1, 32, 8), (8, 12, 4), (4, 64, 2), (2, 96, 3)])
+def test_grouped_matrix_core_target(B, Hq, Hkv, d):
+    """Groups of 3..32 heads: one wave column per K/V head, aiming at the waves whose
+    LDS tiles fit on a CU (10, 5 or 2)."""
+    assert 3 <= Hq // Hkv <= 32
+    assert mfma_waves_per_cu(d) == {32: 10, 64: 10, 96: 5, 128: 5, 256: 2}[d]
+    got = ea.decode_gqa_choose_split(B, Hq, Hkv, 4096, d, 256)
+    assert got == split_rule(B * Hkv, 4096, mfma_waves_per_cu(d) * 256)
+
+
+def test_grouped_headline_chunk():
+    # 8 sequences, 32 query heads over 8 K/V heads of 128: 64 columns aiming at 1280
+    # waves give 192-row chunks (22 splits), the fastest chunk measured for it.
+    assert ea.decode_gqa_choose_split(8, 32, 8, 4096, 128, 256) == (192, 22)
