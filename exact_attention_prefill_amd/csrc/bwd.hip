@@ -50,21 +50,22 @@ constexpr int BN = 64;  // rows of a streamed tile (keys for dQ, query rows for 
 constexpr int NW = 4;   // waves per workgroup, 32 rows (dQ) or keys (dK/dV) each
 }  // namespace bwd_cfg
 
-// Chunk keys of a tile row r (16-byte chunks XOR key).
+// Chunk keys of a tile row r (16-byte chunks XOR key), by LDS row pitch: rows of 256
+// bytes (d = 96, 128) or of 128 bytes (d = 32, 64; lds_row_bytes pads 32 and 96).
 template <int D>
 __device__ __forceinline__ int dual_key(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return lds_row_bytes<D>() == 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int row_key(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return lds_row_bytes<D>() == 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Row operand read (A operand of a 32x32x16 MFMA): lane l gets 16 bytes of tile row
 // (32h + l%32), logical chunk 2ks + l/32.
 template <int D, bool DUAL>
 __device__ __forceinline__ u32x4 row_read(const char* buf, int h, int ks, int lane) {
-  constexpr int RB = 2 * D;
+  constexpr int RB = lds_row_bytes<D>();
   const int row = 32 * h + (lane & 31);
   const int key = DUAL ? dual_key<D>(row & 15) : row_key<D>(row & 15);
   return lds_read_b128((const uint16_t*)buf, row * RB + (((2 * ks + (lane >> 5)) ^ key) << 4));
@@ -76,7 +77,7 @@ __device__ __forceinline__ u32x4 row_read(const char* buf, int h, int ks, int la
 // operand (from a 32x32 accumulator) lists its rows.
 template <int D>
 __device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, int lane) {
-  constexpr int RB = 2 * D;
+  constexpr int RB = lds_row_bytes<D>();
   const int r = lane & 15, gg = (lane >> 4) & 1, half = lane >> 5;
   const int rowlo = 4 * half + (r >> 2);
   const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
@@ -90,23 +91,29 @@ __device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, 
 
 // Stage one BN-row tile of a [rows][D] tensor into LDS: this wave's share of 1 KiB
 // LDS-direct loads; physical slot sl of row r receives logical chunk sl ^ key(r).
+// Padded rows (d = 32, 96) have slots past the data, which take a copy of a chunk of
+// the same row and are never read.
 template <int D, bool DUAL>
 __device__ __forceinline__ void stage_tile(const uint16_t* src, int row0, int rows_total, char* dst, int wave,
                                            int lane) {
   using namespace bwd_cfg;
-  constexpr int RB = 2 * D;
+  constexpr int RBG = 2 * D;                // bytes per row in memory
+  constexpr int RB = lds_row_bytes<D>();    // bytes per row in LDS
+  constexpr int CH = D / 8;
   constexpr int TILE = BN * RB;
   constexpr int NLD = TILE / 1024 / NW;
+  static_assert(NLD >= 1, "tile too small for the load pattern");
   const int left = rows_total - row0;
-  const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * RB;
-  const u32x4 rs = buffer_rsrc((const char*)src + (size_t)row0 * RB, nrec);
+  const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * RBG;
+  const u32x4 rs = buffer_rsrc((const char*)src + (size_t)row0 * RBG, nrec);
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(dst) + wave * NLD * 1024);
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int ci = (wave * NLD + i) * 64 + lane;
     const int row = ci / (RB / 16), sl = ci % (RB / 16);
     const int key = DUAL ? dual_key<D>(row & 15) : row_key<D>(row & 15);
-    lds_dma16(rs, row * RB + ((sl ^ key) << 4), l0 + i * 1024);
+    const int c = sl ^ key;
+    lds_dma16(rs, row * RBG + ((c >= CH ? c - CH : c) << 4), l0 + i * 1024);
   }
 }
 
@@ -120,13 +127,14 @@ __device__ __forceinline__ void pack_unit(const f32x16& x, u32x4 (&pf)[2]) {
 // delta = rowsum(dO * O), D/8 lanes per row.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
+  constexpr int CH = D / 8;                  // 16-byte chunks of a row
+  constexpr int LPR = CH == 12 ? 16 : CH;    // lanes per row (a power of two)
   constexpr int RPB = 256 / LPR;
   const long long total = (long long)p.B * p.H * p.N;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
   const int seg = threadIdx.x % LPR;
   float acc = 0.f;
-  if (row < total) {
+  if (row < total && seg < CH) {
     const u32x4 a = *(const u32x4*)(p.o + row * D + seg * 8);
     const u32x4 b = *(const u32x4*)(p.dout + row * D + seg * 8);
 #pragma unroll
@@ -146,7 +154,7 @@ template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using namespace bwd_cfg;
-  constexpr int RB = 2 * D, KS = D / 16, DB = D / 32, BM = 32 * NW;
+  constexpr int RB = lds_row_bytes<D>(), KS = D / 16, DB = D / 32, BM = 32 * NW;
   constexpr int TILE = BN * RB;
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
@@ -277,11 +285,10 @@ template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using namespace bwd_cfg;
-  constexpr int RB = 2 * D, KS = D / 16, DB = D / 32, BK = 32 * NW;
+  constexpr int RB = lds_row_bytes<D>(), KS = D / 16, DB = D / 32, BK = 32 * NW;
   constexpr int TILE = BN * RB;
   constexpr int NS = 3;       // tile sets in LDS
   constexpr int M = 2 * KS;   // issue slots per pipeline step: one S/dP and one dV/dK MFMA each
-  constexpr int EPS = 16 / M; // softmax-gradient elements per slot
   constexpr int PF = 2;       // operand prefetch distance in slots
   constexpr int R = PF + 1;   // operand ring size
   __shared__ __attribute__((aligned(1024))) char qbuf[NS][TILE];
@@ -446,8 +453,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     f32x4 l4[2], d4[2];  // row groups a and a + 1 (by parity of a)
     grad_rows(gi, 0, l4[0], d4[0]);
     grad_rows(gi, 1, l4[1], d4[1]);
-    float pe[EPS], de[EPS];
     float pp = 0.f, dpp = 0.f;  // the even element of a pair, waiting for its partner
+    float pe = 0.f, de = 0.f;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int j = h * M + i;
@@ -461,23 +468,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int si = (i >> 1) / DB, db = (i >> 1) % DB;
       if (i & 1) dka[db] = mfma32x32x16<DT>(cr[j % R], dsk[h][si], dka[db]);
       else dva[db] = mfma32x32x16<DT>(cr[j % R], pk[h][si], dva[db]);
+      // Slot i takes the unit's elements 16i/M .. 16(i+1)/M - 1 (one at d = 128).
 #pragma unroll
-      for (int q = 0; q < EPS; ++q) {
-        const int e = EPS * i + q;
-        grad_elem(gi, sb, dpb, l4[(e >> 2) & 1], d4[(e >> 2) & 1], e, pe[q], de[q]);
+      for (int e = 16 * i / M; e < 16 * (i + 1) / M; ++e) {
+        grad_elem(gi, sb, dpb, l4[(e >> 2) & 1], d4[(e >> 2) & 1], e, pe, de);
         if (e & 1) {
           const int w = e >> 1;
-          pk[1 - h][w >> 2][w & 3] = pack2<DT>(EPS == 1 ? pp : pe[q - 1], pe[q]);
-          dsk[1 - h][w >> 2][w & 3] = pack2<DT>(EPS == 1 ? dpp : de[q - 1], de[q]);
-        } else if (EPS == 1) {
-          pp = pe[q];
-          dpp = de[q];
+          pk[1 - h][w >> 2][w & 3] = pack2<DT>(pp, pe);
+          dsk[1 - h][w >> 2][w & 3] = pack2<DT>(dpp, de);
+        } else {
+          pp = pe;
+          dpp = de;
         }
         if ((e & 3) == 3 && e < 8) grad_rows(gi, (e >> 2) + 2, l4[(e >> 2) & 1], d4[(e >> 2) & 1]);
       }
       // Anchor the slot's VALU results in the slot (IR-level code motion ignores
       // sched_barrier and would gather the softmax gradient after the MFMAs).
-      asm volatile("" ::"v"(pp), "v"(dpp), "v"(pe[0]), "v"(de[0]));
+      asm volatile("" ::"v"(pp), "v"(dpp), "v"(pe), "v"(de));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(BwdParams p, hipStream_t s) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  constexpr int LPR = D / 8 == 12 ? 16 : D / 8, RPB = 256 / LPR;  // as bwd_delta_kernel
   const long long rows = (long long)p.B * p.H * p.N;
   hipLaunchKernelGGL((bwd_delta_kernel<DT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
@@ -583,14 +590,16 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   p.scale = scale;
 #define ATTN_BW(DT_, D_, C_) \
   if (dt == DT_ && d == D_ && causal == C_) return launch_bwd_t<DT_, D_, C_>(p, s);
-  ATTN_BW(DT_F16, 64, false)
-  ATTN_BW(DT_F16, 64, true)
-  ATTN_BW(DT_F16, 128, false)
-  ATTN_BW(DT_F16, 128, true)
-  ATTN_BW(DT_BF16, 64, false)
-  ATTN_BW(DT_BF16, 64, true)
-  ATTN_BW(DT_BF16, 128, false)
-  ATTN_BW(DT_BF16, 128, true)
+#define ATTN_BW_D(D_)         \
+  ATTN_BW(DT_F16, D_, false)  \
+  ATTN_BW(DT_F16, D_, true)   \
+  ATTN_BW(DT_BF16, D_, false) \
+  ATTN_BW(DT_BF16, D_, true)
+  ATTN_BW_D(64)
+  ATTN_BW_D(128)
+  ATTN_BW_D(32)
+  ATTN_BW_D(96)
+#undef ATTN_BW_D
 #undef ATTN_BW
   return hipErrorInvalidValue;
 }

@@ -41,7 +41,7 @@ def parity(B, Hq, Hkv, N, d, dtype, causal, scale, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 130, 257])
 def test_backward_parity(N, causal, d, dtype):
@@ -52,12 +52,13 @@ def test_backward_parity(N, causal, d, dtype):
 @pytest.mark.parametrize("heads", [(4, 2), (6, 1), (8, 8)], ids=lambda h: f"hq{h[0]}_hkv{h[1]}")
 def test_backward_grouped_heads(heads, causal):
     parity(2, heads[0], heads[1], 200, 128, "bf16", causal, 0.0884, seed=heads[0])
+    parity(1, heads[0], heads[1], 150, 96, "f16", causal, 0.1, seed=heads[0] + 1)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 def test_backward_many_tiles(d, causal):
-    parity(1, 4, 2, 700, d, "f16" if d == 64 else "bf16", causal, 1 / np.sqrt(d), seed=7)
+    parity(1, 4, 2, 700, d, "f16" if d in (32, 64) else "bf16", causal, 1 / np.sqrt(d), seed=7)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
