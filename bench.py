@@ -240,6 +240,20 @@ def main():
     gqa_gbs = gqa_bytes / (gqa_us * 1e-6) / 1e9
     log(f"decode (grouped heads {GQ.H}/{gkv}) cold {gqa_us:.2f} us = {gqa_gbs:.0f} GB/s")
 
+    # The prefill with its row log-sum-exp output (the forward the backward pass needs),
+    # timed like the step's prefill.
+    lse_buf = torch.empty(P.B, P.H, P.N, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out, lse=lse_buf)
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in lev:
+        a.record()
+        ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out, lse=lse_buf)
+        b.record()
+    torch.cuda.synchronize()
+    lse_ms = float(np.median([a.elapsed_time(b) for a, b in lev]))
+    log(f"prefill with lse {lse_ms:.3f} ms = {P.flop / (lse_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+
     # Backward pass at the prefill's shape (out and lse from the forward with the
     # log-sum-exp output, a seeded dout), timed with events outside the step.
     bdo = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=1)[0].to(dev)
@@ -273,13 +287,13 @@ def main():
             hout = torch.empty_like(hq)
             for _ in range(2):
                 ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
-            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
             for a, b in hev:
                 a.record()
                 ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
                 b.record()
             torch.cuda.synchronize()
-            hms = float(np.mean([a.elapsed_time(b) for a, b in hev]))
+            hms = float(np.median([a.elapsed_time(b) for a, b in hev]))
             htf = 4.0 * P.B * P.H * P.N * P.N * hd / (hms * 1e-3) / 1e12
             head_sizes[str(hd)] = {"ms": round(hms, 4), "tflops": round(htf, 1), "frac": round(htf / PEAK_BF16_TFLOPS, 4)}
             del hq, hk, hv, hout
@@ -368,6 +382,7 @@ def main():
             "config": {"B": GQ.B, "Hq": GQ.H, "Hkv": gkv, "max_len": GQ.max_len, "d": GQ.d, "dtype": GQ.dtype,
                        "seq_lens": gl.tolist(), "chunk": gchunk, "n_split": gns},
         },
+        "prefill_lse": {"ms": round(lse_ms, 4), "tflops": round(P.flop / (lse_ms * 1e-3) / 1e12, 1)},
         "backward": {
             "bound": "mfma",
             "achieved": round(bwd_tflops, 2),

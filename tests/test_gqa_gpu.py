@@ -153,3 +153,16 @@ def test_gqa_python_errors():
     k = torch.zeros(1, 4, 8, 64, dtype=torch.float16, device=DEV)
     with pytest.raises(ValueError):
         ea.prefill(q, k, k.clone())
+
+
+@pytest.mark.parametrize("max_len", [1, 5, 31, 32, 33, 64, 65])
+@pytest.mark.parametrize("g", [4, 32])
+def test_decode_gqa_short_caches(g, max_len):
+    """Caches shorter than one 32-row tile, or one row past it, on the matrix-core path:
+    partial tiles start from zeroed LDS and their missing rows weigh nothing."""
+    B, Hkv = 3, 2
+    lens = [max_len, 1, max(1, max_len // 2)]
+    q, kc, vc, lens = W.decode_inputs_gqa(B, g * Hkv, Hkv, max_len, 128, "bf16", seed=max_len, seq_lens=lens)
+    out = ea.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV), scale=0.09)
+    torch.cuda.synchronize()
+    check(f64(out), oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), 0.09), "bf16", f"short g={g} L={max_len}")
