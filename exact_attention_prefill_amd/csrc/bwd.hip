@@ -18,8 +18,9 @@
 //     heads, so a K/V head's gradient sums theirs.
 // Tiles staged through LDS are read both as row operands (ds_read_b128) and through
 // transpose loads, so their 16-byte chunks carry a key that is conflict-free for both
-// (verified with the LDS bank-conflict counter): d = 128: ((r&3)<<2) | ((r>>2)&3);
-// d = 64: (((r>>1)&1)<<2) | ((r>>2)&3).  Tiles read only as row operands keep the
+// (verified with the LDS bank-conflict counter): rows of 256 bytes (d = 128, and
+// d = 96 padded): ((r&3)<<2) | ((r>>2)&3); rows of 128 bytes (d = 64, and d = 32
+// padded): (((r>>1)&1)<<2) | ((r>>2)&3).  Tiles read only as row operands keep the
 // forward's K key.  P and dS enter the matrix cores rounded to the input type (RNE),
 // as P does in the forward.
 #include <type_traits>

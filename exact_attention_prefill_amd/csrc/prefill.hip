@@ -65,9 +65,10 @@ constexpr int prefill_waves_per_simd() {
 }
 
 // NW waves per workgroup, each owning QB blocks of 32 query rows.  QB = 1: two waves
-// share each SIMD (<= 256 registers, up to d = 128).  QB = 2: the two row blocks share every K and V
-// operand read, halving LDS traffic per MFMA; a wave then needs ~350 registers, so
-// one wave runs per SIMD with the MFMA accumulators in AGPRs.
+// share each SIMD (<= 256 registers) up to d = 128; d = 256 runs one wave per SIMD.
+// QB = 2: the two row blocks share every K and V operand read, halving LDS traffic
+// per MFMA; a wave then needs ~350 registers, so one wave runs per SIMD with the MFMA
+// accumulators in AGPRs.
 template <int DT, int D, bool CAUSAL, int NW, int QB>
 __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub

@@ -13,6 +13,9 @@
  *                  KV cache whose current length differs per sequence, computed as a
  *                  split-K pass that writes partial (m, l, acc) per chunk, then an
  *                  exact merge pass with no atomics (page 3, "Kernel design").
+ * Page 3's "Future work" items built on the same kernels: grouped K/V heads
+ * (attn_prefill_gqa, attn_decode_gqa), the row log-sum-exp (attn_prefill_ex), the
+ * backward pass (attn_backward) and head dimensions 32, 96 and 256 beside 64 and 128.
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major (batch, heads, rows, d) with d fastest, no strides.
