@@ -22,7 +22,7 @@ bool decode_uses_mfma(int H, int Hkv);
 int decode_mfma_waves_per_cu(int d);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
-                           int d, int dt, int causal, float scale, hipStream_t s);
+                           int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
 }  // namespace attn
 
 namespace {
@@ -204,6 +204,10 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
   if (workspace && !aligned16(workspace)) return fail(ATTN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
   if (!workspace && ws_bytes != 0) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but ws_bytes > 0");
   const size_t need = attn_backward_workspace_bytes(B, Hq, N);
+  if (workspace && ws_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  int cus = 0;
+  if ((st = device_cus(&cus)) != ATTN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   bool own = false;
@@ -211,11 +215,9 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
     hipError_t e = hipMallocAsync(&ws, need, s);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", need, hipGetErrorString(e));
     own = true;
-  } else if (ws_bytes < need) {
-    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
   }
   hipError_t e = attn::launch_backward(q, k, v, out, dout, lse, (float*)ws, dq, dk, dv, B, Hq, Hkv, N, d, dtype, causal,
-                                       scale, s);
+                                       scale, cus, s);
   if (own) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;

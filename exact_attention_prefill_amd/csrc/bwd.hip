@@ -48,7 +48,7 @@ struct BwdParams {
 
 namespace bwd_cfg {
 constexpr int BN = 64;  // rows of a streamed tile (keys for dQ, query rows for dK/dV)
-constexpr int NW = 4;   // waves per workgroup, 32 rows (dQ) or keys (dK/dV) each
+constexpr int NW = 4;   // waves per dK/dV workgroup, 32 keys each
 }  // namespace bwd_cfg
 
 // Chunk keys of a tile row r (16-byte chunks XOR key), by LDS row pitch: rows of 256
@@ -94,10 +94,10 @@ __device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, 
 // LDS-direct loads; physical slot sl of row r receives logical chunk sl ^ key(r).
 // Padded rows (d = 32, 96) have slots past the data, which take a copy of a chunk of
 // the same row and are never read.
-template <int D, bool DUAL>
+template <int D, bool DUAL, int NW = bwd_cfg::NW>
 __device__ __forceinline__ void stage_tile(const uint16_t* src, int row0, int rows_total, char* dst, int wave,
                                            int lane) {
-  using namespace bwd_cfg;
+  constexpr int BN = bwd_cfg::BN;
   constexpr int RBG = 2 * D;                // bytes per row in memory
   constexpr int RB = lds_row_bytes<D>();    // bytes per row in LDS
   constexpr int CH = D / 8;
@@ -151,10 +151,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------------
 // dQ: workgroup = 128 query rows of one (b, h); tiles of 64 keys.
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+template <int DT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using namespace bwd_cfg;
+  constexpr int BN = bwd_cfg::BN;
   constexpr int RB = lds_row_bytes<D>(), KS = D / 16, DB = D / 32, BM = 32 * NW;
   constexpr int TILE = BN * RB;
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
@@ -211,11 +211,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  stage_tile<D, true>(kg, 0, N, kbuf0, wave, lane);
-  stage_tile<D, false>(vg, 0, N, vbuf0, wave, lane);
+  stage_tile<D, true, NW>(kg, 0, N, kbuf0, wave, lane);
+  stage_tile<D, false, NW>(vg, 0, N, vbuf0, wave, lane);
   if (nt > 1) {
-    stage_tile<D, true>(kg, BN, N, kbuf1, wave, lane);
-    stage_tile<D, false>(vg, BN, N, vbuf1, wave, lane);
+    stage_tile<D, true, NW>(kg, BN, N, kbuf1, wave, lane);
+    stage_tile<D, false, NW>(vg, BN, N, vbuf1, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 2 < nt) {
-      stage_tile<D, true>(kg, (t + 2) * BN, N, kb, wave, lane);
-      stage_tile<D, false>(vg, (t + 2) * BN, N, vb, wave, lane);
+      stage_tile<D, true, NW>(kg, (t + 2) * BN, N, kb, wave, lane);
+      stage_tile<D, false, NW>(vg, (t + 2) * BN, N, vb, wave, lane);
     }
   }
 
@@ -550,18 +550,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #endif
 }
 
+// dQ with NWQ waves of 32 query rows per workgroup.
+template <int DT, int D, bool CAUSAL, int NWQ>
+static hipError_t launch_dq(BwdParams p, hipStream_t s) {
+  p.nblk = (p.N + 32 * NWQ - 1) / (32 * NWQ);
+  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL, NWQ>), dim3((unsigned)((long long)p.nblk * p.B * p.H)),
+                     dim3(64 * NWQ), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int DT, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(BwdParams p, hipStream_t s) {
+static hipError_t launch_bwd_t(BwdParams p, int num_cus, hipStream_t s) {
   constexpr int LPR = D / 8 == 12 ? 16 : D / 8, RPB = 256 / LPR;  // as bwd_delta_kernel
   const long long rows = (long long)p.B * p.H * p.N;
   hipLaunchKernelGGL((bwd_delta_kernel<DT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Eight-wave dQ workgroups (256 rows, one per CU) stage each K/V tile for twice the
+  // rows; as in the prefill they pay (about 2% at 16K tokens) once the grid gives every
+  // CU four of them, and smaller grids keep four waves.
+  const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
+  e = blocks8 >= 4LL * num_cus ? launch_dq<DT, D, CAUSAL, 8>(p, s) : launch_dq<DT, D, CAUSAL, 4>(p, s);
+  if (e != hipSuccess) return e;
   const int blk = 32 * bwd_cfg::NW;
   p.nblk = (p.N + blk - 1) / blk;
-  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.H)),
-                     dim3(64 * bwd_cfg::NW), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.Hkv)),
                      dim3(64 * bwd_cfg::NW), 0, s, p);
   return hipGetLastError();
@@ -569,7 +581,7 @@ static hipError_t launch_bwd_t(BwdParams p, hipStream_t s) {
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
-                           int d, int dt, int causal, float scale, hipStream_t s) {
+                           int d, int dt, int causal, float scale, int num_cus, hipStream_t s) {
   BwdParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -590,7 +602,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   p.c = scale * kLog2e;
   p.scale = scale;
 #define ATTN_BW(DT_, D_, C_) \
-  if (dt == DT_ && d == D_ && causal == C_) return launch_bwd_t<DT_, D_, C_>(p, s);
+  if (dt == DT_ && d == D_ && causal == C_) return launch_bwd_t<DT_, D_, C_>(p, num_cus, s);
 #define ATTN_BW_D(D_)         \
   ATTN_BW(DT_F16, D_, false)  \
   ATTN_BW(DT_F16, D_, true)   \

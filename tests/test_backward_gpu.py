@@ -117,3 +117,30 @@ def test_backward_headline_sampled(causal):
         check_grad(f64(dv[0, h, rows]), rv, bv, P.dtype, "dv " + what)
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_eight_wave_dq_sampled(causal):
+    """64 query heads over 8 K/V heads at 4000 tokens: enough 256-row blocks for the
+    eight-wave dQ workgroups, with a ragged last block; sampled dq rows and dk/dv key
+    rows against the row-sampled oracle."""
+    from parity import backward_bounds_keys, backward_bounds_rows
+
+    B, Hq, Hkv, N, d = 1, 64, 8, 4000, 128
+    scale = 1 / np.sqrt(d)
+    q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=31)
+    dout = W.prefill_inputs(B, Hq, N, d, "bf16", seed=32)[0]
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=scale, lse=True)
+    dq, dk, dv = ea.backward(qd, kd, vd, out, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    qf, kf, vf, df = (f64(t) for t in (q, k, v, dout))
+    rows = W.prefill_rows_sample(N, 10, seed=33)
+    for h in (0, 63):
+        ref = oracle.backward_dq_rows(qf, kf, vf, df, causal, scale, 0, h, rows)
+        bq = backward_bounds_rows(qf, kf, vf, df, causal, scale, 0, h, rows)
+        check_grad(f64(dq[0, h, rows]), ref, bq, "bf16", f"dq h={h} causal={causal}")
+    rk, rv = oracle.backward_dkdv_rows(qf, kf, vf, df, causal, scale, 0, 7, rows)
+    bk, bv = backward_bounds_keys(qf, kf, vf, df, causal, scale, 0, 7, rows)
+    check_grad(f64(dk[0, 7, rows]), rk, bk, "bf16", f"dk causal={causal}")
+    check_grad(f64(dv[0, 7, rows]), rv, bv, "bf16", f"dv causal={causal}")
