@@ -21,7 +21,7 @@ int decode_heads_per_wave(int H, int Hkv);
 bool decode_uses_mfma(int H, int Hkv);
 int decode_mfma_waves_per_cu(int d);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                           const float* lse, float* ws, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
                            int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
 }  // namespace attn
 
@@ -178,7 +178,7 @@ int attn_decode_choose_split(int B, int H, int max_len, int d, int num_cus, int*
 
 size_t attn_backward_workspace_bytes(int B, int Hq, int N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
-  return (size_t)B * Hq * N * sizeof(float);
+  return 2 * (size_t)B * Hq * N * sizeof(float);
 }
 
 int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,

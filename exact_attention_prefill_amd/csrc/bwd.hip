@@ -37,6 +37,7 @@ struct BwdParams {
   const uint16_t* dout;
   const float* lse;  // [B][H][N] natural log
   float* delta;      // [B][H][N] rowsum(dO * O), written by the pre-pass
+  float* lse2;       // [B][H][N] lse * log2(e), written by the pre-pass
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -125,7 +126,8 @@ __device__ __forceinline__ void pack_unit(const f32x16& x, u32x4 (&pf)[2]) {
 }
 
 // ---------------------------------------------------------------------------------
-// delta = rowsum(dO * O), D/8 lanes per row.
+// delta = rowsum(dO * O), D/8 lanes per row; beside it lse * log2(e), the row's
+// log-sum-exp in the base-2 domain the gradient kernels exponentiate in.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   constexpr int CH = D / 8;                  // 16-byte chunks of a row
@@ -146,7 +148,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < total && seg == 0) p.delta[row] = acc;
+  if (row < total && seg == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
       df[ks] = *(const u32x4*)(p.dout + off);
     }
   }
-  const float lse2 = row_ok ? p.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : 0.f;
   const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.f;
 
   f32x16 dqa[DB];
@@ -220,6 +225,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // Keys visible to this lane's row: below N and (causal) at most the row.
+  const int key_end = CAUSAL ? min(N, qrow + 1) : N;
   auto unit = [&](int u, const char* kb, const char* vb, int h) __attribute__((always_inline)) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
@@ -228,12 +235,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
       dpt = mfma32x32x16<DT>(row_read<D, false>(vb, h, ks, lane), df[ks], dpt);
     }
     f32x16 ds;
+    // Entry i holds key 32u + 4half + 8(i/4) + i%4: visible iff its offset 8(i/4) + i%4
+    // (a constant) is below lim.
+    const int lim = key_end - 32 * u - 4 * half;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = 32 * u + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool ok = key < N && (!CAUSAL || key <= qrow);
-      const float pr = fast_exp2(p.c * st[i] - lse2);
-      ds[i] = ok ? pr * (dpt[i] - dl) : 0.f;
+      const float pr = fast_exp2(__builtin_fmaf(st[i], p.c, -lse2));
+      ds[i] = 8 * (i >> 2) + (i & 3) < lim ? pr * (dpt[i] - dl) : 0.f;
     }
     u32x4 dsf[2];
     pack_unit<DT>(ds, dsf);
@@ -357,8 +365,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     stage_tile<D, true>(p.dout + (size_t)bh * N * D, row0, N, dbuf[set], wave, lane);
     if (wave == 0) {
       const int left = N - row0;
+      // Rows past N take lse = +inf, so their P (and dS) is exactly 0 without a test;
+      // the loads below write only rows < left.
+      if (lane >= left) lsebuf[set][lane] = INFINITY;
       const uint32_t nrec = (uint32_t)(left < BN ? left : BN) * 4;
-      const u32x4 rl = buffer_rsrc(p.lse + (size_t)bh * N + row0, nrec);
+      const u32x4 rl = buffer_rsrc(p.lse2 + (size_t)bh * N + row0, nrec);
       const u32x4 rd = buffer_rsrc(p.delta + (size_t)bh * N + row0, nrec);
       lds_dma4(rl, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&lsebuf[set][0])));
       lds_dma4(rd, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&dlbuf[set][0])));
@@ -367,21 +378,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto row0_of = [&](int n) __attribute__((always_inline)) { return r_start + (n % nt) * BN; };
 
   // Softmax gradient of one unit, element by element.  Accumulator entry i of lane l
-  // is (row 8(i/4) + 4(l/32) + i%4 of the unit, key l%32).  Rows past N and (causal)
-  // rows before the key get x = -inf, so P = 0 and dS = 0 exactly.
-  const int kk = CAUSAL ? key : 0;
-  const uint32_t lim = (uint32_t)(N - kk);
+  // is (row 8(i/4) + 4(l/32) + i%4 of the unit, key l%32).  Rows past N carry lse =
+  // +inf (see stage), and under the causal mask rows before the key get x = -inf, so
+  // P = 0 and dS = 0 exactly.
   struct GradIn {
     const float* lse;
     const float* dl;
-    int rb;  // unit row of entry 0 for this lane half, minus kk
+    int lo;  // causal: entries whose row offset 8(i/4) + i%4 is below lo precede the key
   };
   auto grad_in = [&](int n, int hb) __attribute__((always_inline)) {
     const int set = n % NS;
     GradIn g;
     g.lse = &lsebuf[set][32 * hb];
     g.dl = &dlbuf[set][32 * hb];
-    g.rb = row0_of(n) + 32 * hb + 4 * half - kk;
+    g.lo = key - (row0_of(n) + 32 * hb + 4 * half);
     return g;
   };
   auto grad_rows = [&](const GradIn& g, int a, f32x4& l4, f32x4& d4) __attribute__((always_inline)) {
@@ -391,9 +401,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto grad_elem = [&](const GradIn& g, const f32x16& s, const f32x16& dp, const f32x4& l4, const f32x4& d4,
                        int i, float& pm, float& ds) __attribute__((always_inline)) {
     const int e = i & 3;
-    const bool ok = (uint32_t)(g.rb + 8 * (i >> 2) + e) < lim;
-    float x = __builtin_fmaf(s[i], p.c, -l4[e] * kLog2e);
-    x = ok ? x : -INFINITY;
+    float x = __builtin_fmaf(s[i], p.c, -l4[e]);
+    if (CAUSAL) x = 8 * (i >> 2) + e >= g.lo ? x : -INFINITY;
     pm = fast_exp2(x);
     ds = pm * (dp[i] - d4[e]);
   };
@@ -446,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     GradIn gi;
     gi.lse = &lsebuf[SB][32 * (1 - h)];
     gi.dl = &dlbuf[SB][32 * (1 - h)];
-    gi.rb = row0_of(n + h) + 32 * (1 - h) + 4 * half - kk;
+    gi.lo = key - (row0_of(n + h) + 32 * (1 - h) + 4 * half);
     f32x16& sn = sacc[h];
     f32x16& dpn = dpacc[h];
     const f32x16& sb = sacc[1 - h];
@@ -580,7 +589,7 @@ static hipError_t launch_bwd_t(BwdParams p, int num_cus, hipStream_t s) {
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                           const float* lse, float* ws, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
                            int d, int dt, int causal, float scale, int num_cus, hipStream_t s) {
   BwdParams p;
   p.q = (const uint16_t*)q;
@@ -589,7 +598,8 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   p.o = (const uint16_t*)o;
   p.dout = (const uint16_t*)dout;
   p.lse = lse;
-  p.delta = delta;
+  p.delta = ws;
+  p.lse2 = ws + (size_t)B * H * N;
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;

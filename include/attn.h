@@ -179,7 +179,8 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int dtype, int causal,
                   float scale, void* workspace, size_t ws_bytes, void* stream);
 
-/* Host-only: workspace bytes of attn_backward (one fp32 per query row). */
+/* Host-only: workspace bytes of attn_backward (two fp32 per query row: rowsum(dout *
+ * out) and lse * log2(e), written by its pre-pass). */
 size_t attn_backward_workspace_bytes(int B, int Hq, int N);
 
 /* Host-only: bytes of decode workspace for B*H*n_split partials of (m, l, acc[d]) fp32. */

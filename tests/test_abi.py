@@ -254,5 +254,5 @@ def test_backward_validation(kw, status):
 
 
 def test_backward_workspace_bytes():
-    assert ea.backward_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert ea.backward_workspace_bytes(2, 8, 100) == 2 * (2 * 8 * 100 * 4)
     assert ea.backward_workspace_bytes(0, 8, 100) == 0
