@@ -136,9 +136,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
       const int row = base + u * RPW + rsub;
       kr[u] = (u32x4){0, 0, 0, 0};
       vr[u] = (u32x4){0, 0, 0, 0};
-      if (row < r1 && seg_ok) {
-        kr[u] = *(const u32x4*)(kg + (size_t)row * D);
-        vr[u] = *(const u32x4*)(vg + (size_t)row * D);
+      if (row < r1 && seg_ok) {  // read once: non-temporal, so the stream does not displace other lines
+        kr[u] = __builtin_nontemporal_load((const u32x4*)(kg + (size_t)row * D));
+        vr[u] = __builtin_nontemporal_load((const u32x4*)(vg + (size_t)row * D));
       }
     }
   };
@@ -218,6 +218,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
     }
   }
 }
+
+// lds_dma16 with the non-temporal policy: cache rows are read once, so their lines
+// need not stay in the caches.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_nt(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %0, 0 offen nt lds"
+      :
+      : "s"(rsrc), "v"(voff), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Grouped heads on the matrix cores.  One wave per (split, K/V head, batch) scores
 // all g query heads of the group at once: they are the columns of one 32-wide MFMA
@@ -322,9 +337,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeParams p) {
     const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr_of(kb));
     const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr_of(vb));
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_dma16(rk, ldk_off[i], lk + i * 1024);
+    for (int i = 0; i < NLD; ++i) lds_dma16_nt(rk, ldk_off[i], lk + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_dma16(rv, ldv_off[i], lv + i * 1024);
+    for (int i = 0; i < NLD; ++i) lds_dma16_nt(rv, ldv_off[i], lv + i * 1024);
   };
 
   f32x16 oacc[DB];
