@@ -251,9 +251,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
       for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(tr_read<D>(kb, h, s, db, lane), dsf[s], dqa[db]);
   };
 
-  for (int t = 0; t < nt; ++t) {
-    char* kb = (t & 1) ? kbuf1 : kbuf0;
-    char* vb = (t & 1) ? vbuf1 : vbuf0;
+  // Tile t from (kb, vb); the loop is unrolled over the two buffer pairs so that every
+  // LDS read addresses a compile-time buffer (its base folds into the offset).
+  auto tile = [&](int t, char* kb, char* vb) __attribute__((always_inline)) {
     if (2 * t < nu_w) unit(2 * t, kb, vb, 0);
     if (2 * t + 1 < nu_w) unit(2 * t + 1, kb, vb, 1);
     __builtin_amdgcn_s_waitcnt(0);
@@ -262,6 +262,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
       stage_tile<D, true, NW>(kg, (t + 2) * BN, N, kb, wave, lane);
       stage_tile<D, false, NW>(vg, (t + 2) * BN, N, vb, wave, lane);
     }
+  };
+  for (int t = 0; t < nt; t += 2) {
+    tile(t, kbuf0, vbuf0);
+    if (t + 1 < nt) tile(t + 1, kbuf1, vbuf1);
   }
 
   if (row_ok) {
