@@ -146,3 +146,18 @@ def test_workspace_too_small_raises():
     with pytest.raises(ea.AttnError) as e:
         ea.decode(q, kc, vc, lens, chunk=64, workspace=ws)
     assert e.value.status == ea.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("heads", [(4, 4), (16, 4)], ids=["mha", "grouped"])
+def test_long_cache_many_splits(heads):
+    """A 65536-row cache: hundreds of splits per sequence, so the merge runs several
+    rounds, on both split kernels (vector ALUs, and the matrix cores for the group)."""
+    Hq, Hkv = heads
+    B, max_len, d = 2, 65536, 128
+    q, kc, vc, lens = W.decode_inputs_gqa(B, Hq, Hkv, max_len, d, "bf16", seed=77, seq_lens=[65536, 40001])
+    out = ea.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV), scale=1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    chunk, n_split = ea.decode_gqa_choose_split(B, Hq, Hkv, max_len, d, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert n_split >= 64, (chunk, n_split)
+    ref = oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), 1 / np.sqrt(d))
+    check(f64(out), ref, "bf16", f"long cache {heads} chunk={chunk} n_split={n_split}")

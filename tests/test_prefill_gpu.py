@@ -188,3 +188,10 @@ def test_python_errors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
     with pytest.raises(ValueError):
         ea.prefill(q, q.clone(), q.clone())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_short_sequences(causal):
+    """A large batch of short sequences (32 x 8 heads x 65 rows): batch and head indexing
+    across many workgroups, each with a ragged last tile."""
+    full_parity(32, 8, 65, 64, "f16", causal, 0.125, seed=12)
