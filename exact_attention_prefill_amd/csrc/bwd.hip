@@ -4,7 +4,8 @@
 // P = exp(scale q.k - lse) from the row log-sum-exp the forward wrote
 // (attn_prefill_ex), so P is the forward's exact normalised probability.
 //
-//   delta_i = sum_d dO_id O_id                     (pre-pass, one value per row)
+//   delta_i = sum_d dO_id O_id                     (pre-pass, one value per row,
+//                                                   beside lse_i log2(e))
 //   dS      = P * (dO V^T - delta)                 (elementwise, rows x keys)
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
 //
