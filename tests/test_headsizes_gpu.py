@@ -162,3 +162,19 @@ def test_prefill_causality_and_canaries(d):
     assert torch.equal(buf[:guard], canary) and torch.equal(buf[-guard:], canary)
     assert torch.isfinite(a).all()
     assert torch.equal(a[:, :, : i + 1].view(torch.int16), b[:, :, : i + 1].view(torch.int16))
+
+
+@pytest.mark.parametrize("d", NEW_D)
+def test_prefill_sixteen_k_sampled(d):
+    """16384 tokens, as the benchmark's head-size sweep runs them: sampled rows of the
+    first and last heads against the row-sampled oracle."""
+    B, H, N = 1, 4, 16384
+    scale = 1 / np.sqrt(d)
+    q, k, v = W.prefill_inputs(B, H, N, d, "bf16", seed=d + 3)
+    out = ea.prefill(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale)
+    torch.cuda.synchronize()
+    rows = W.prefill_rows_sample(N, 16, seed=d)
+    for h in (0, H - 1):
+        ref = oracle.prefill_rows(f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1]), False, scale, 0, 0, rows)
+        check(f64(out[0, h, rows]), ref, "bf16", f"d={d} N=16384 h={h}")
+    assert torch.isfinite(out).all()
