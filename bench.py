@@ -24,6 +24,11 @@ the prefill's shape, also outside the steps; its flop count is 2.5 times the
 forward's (the five products of the chain rule, each of the forward's size).
 `head_sizes` times the prefill at d = 32, 64, 96, 128 and 256 with the headline's
 B, H and N (bf16, non-causal), outside the steps.
+`configs` times every other workload shape alone, outside the steps: the small
+prefill (B=1, H=1, N=128, d=64, fp16), the GPT-2-like prompt (B=1, H=12, N=2048, d=64,
+fp16, full and causal), the dense d=128 token splits (B*N = 16384 at H=16), the long
+sequences (B=1, H=24, d=128, bf16: N=32768 full, N=16384 causal) and the batch-1
+decode over a full 4096-row cache, cold like the step's decode.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
 """
 
@@ -121,6 +126,7 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=100)
     ap.add_argument("--bwd-iters", type=int, default=10)
     ap.add_argument("--no-head-sizes", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing every workload shape")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument(
@@ -299,6 +305,42 @@ def main():
             del hq, hk, hv, hout
         log("head sizes: " + ", ".join(f"d={k} {v['tflops']} TF" for k, v in head_sizes.items()))
 
+    # Every prefill workload shape (small, GPT-2-like at 2048 tokens, the dense d=128
+    # token splits, the long sequences) and the batch-1 decode, each timed alone with
+    # events: median of 5 launches after 2 warm-ups; decode cold as above.
+    configs = {}
+    if not args.no_configs:
+        for case in W.SMALL_F16 + W.GPT2_F16 + W.DENSE_D128 + W.LONG:
+            cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=0))
+            cout = torch.empty_like(cq)
+            for _ in range(2):
+                ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, b in cev:
+                a.record()
+                ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)
+                b.record()
+            torch.cuda.synchronize()
+            cms = float(np.median([a.elapsed_time(b) for a, b in cev]))
+            ctf = case.flop / (cms * 1e-3) / 1e12
+            configs[case.name] = {"ms": round(cms, 4), "tflops": round(ctf, 1), "frac": round(ctf / PEAK_BF16_TFLOPS, 4)}
+            del cq, ck, cv, cout
+        D1 = W.DECODE[0]
+        eq, ek, ev_, el = (t.to(dev) for t in W.decode_inputs(D1.B, D1.H, D1.max_len, D1.d, D1.dtype, seed=0))
+        eout = torch.empty_like(eq)
+        echunk, ens = ea.decode_choose_split(D1.B, D1.H, D1.max_len, D1.d, cus)
+        ews = torch.empty(ea.decode_workspace_bytes(D1.B, D1.H, ens, D1.d), dtype=torch.uint8, device=dev)
+        ecall = lambda: ea.decode(eq, ek, ev_, el, scale=D1.scale, out=eout, chunk=echunk, workspace=ews)  # noqa: E731
+        for _ in range(3):
+            ecall()
+        eus = cold_us_of(ecall, args.decode_iters)
+        ebytes = W.decode_bytes(D1.H, D1.d, el.cpu().tolist())
+        egbs = ebytes / (eus * 1e-6) / 1e9
+        configs[D1.name] = {"us_cold": round(eus, 3), "gbs": round(egbs, 1), "frac": round(egbs / PEAK_HBM_GBS, 4),
+                            "bytes": ebytes, "chunk": echunk, "n_split": ens}
+        del eq, ek, ev_, eout, ews
+        log("configs: " + ", ".join(f"{k} {v.get('tflops', v.get('gbs'))}" for k, v in configs.items()))
+
     # Parity spot check of this run's outputs against the oracle (sampled rows).
     import oracle
 
@@ -394,6 +436,7 @@ def main():
             "config": {"B": P.B, "H": P.H, "N": P.N, "d": P.d, "dtype": P.dtype, "causal": P.causal},
         },
         "head_sizes": {"config": f"prefill B={P.B} H={P.H} N={P.N} bf16 non-causal", "by_d": head_sizes},
+        "configs": configs,
         "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr,
                    "backward_dq_sampled_max_err": berr},
         "cpu_baseline": cpu,

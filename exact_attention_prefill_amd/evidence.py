@@ -1,0 +1,387 @@
+"""rocprofv3 evidence for the attention kernels on one MI355X.
+
+    python -m exact_attention_prefill_amd.evidence --out DIR [--passes trace,fetch,write,mfma,lds,wave]
+    python -m exact_attention_prefill_amd.evidence --out DIR --summarize-only
+
+Runs ``bench.py`` under rocprofv3 once per pass -- a kernel trace, then one counter set
+per run, because rocprofv3 collects a set in a single pass and refuses sets that exceed
+a hardware block's counter slots -- and then reads the CSV files back and writes
+``DIR/summary.md`` and ``DIR/prefill_headline_counters.json`` (the HBM traffic figure
+``bench.py`` reports while the prefill sources hash to the same value).
+
+What it derives, per attention kernel:
+
+* dispatch time from the kernel trace.  The headline prefill (B=1, H=16, N=16384,
+  d=128, bf16, full) is rated in TFLOP/s (4*B*H*N*N*d per launch) against the
+  2.5 PFLOP/s dense bf16 peak; the ragged decode (B=8, H=12, d=64, fp16) in GB/s
+  (K and V rows read, q and out) over split + merge, against 8 TB/s;
+* HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+  counter reads for a plain device copy of known size made in the same process
+  (``bench.py --calibrate-copy``);
+* MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES over (SIMDs x cycles), with the cycles
+  from GRBM_GUI_ACTIVE per XCD and the clock from those cycles over the dispatch
+  time, cross-checked by the instruction count (SQ_INSTS_MFMA x 32 cycles for the
+  32x32x16 MFMA every one of these kernels uses).
+
+The parent process never touches the GPU: every pass is a child process, and the
+program follows rocprofv3's ``--`` directly (the Python interpreter, no launcher).
+A pass that fails ends the run; nothing is retried.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "exact_attention_prefill_amd", "csrc")
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+MFMA_CYCLES = 32  # v_mfma_f32_32x32x16_{bf16,f16}: 8 passes of 4 cycles
+CALIBRATE_MIB = 256
+MIN_CLOCK_NS = 100_000  # shortest dispatch whose clock is derived
+
+# bench.py arguments per pass: the trace pass times more launches; counter passes run a
+# few (every dispatch is replayed per counter set).
+TRACE_STEPS, TRACE_WARMUP, TRACE_DECODE_ITERS = 10, 2, 20
+PMC_STEPS, PMC_WARMUP, PMC_DECODE_ITERS = 3, 1, 3
+
+COUNTER_SETS = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "mfma": ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+             "SQ_WAVES", "SQ_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES"],
+    "lds": ["SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS",
+            "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"],
+    "wave": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS",
+             "SQ_ACTIVE_INST_MISC", "GRBM_GUI_ACTIVE"],
+}
+ALL_PASSES = ["trace"] + list(COUNTER_SETS)
+
+# Counter slots per hardware block on this part (one pass), and the slots a derived
+# counter takes.  A set beyond these makes rocprofv3 report "exceeds the capabilities"
+# and stall, so sets are checked before any run.
+BLOCK_SLOTS = {"SQ": 8, "TCC": 4, "TCP": 4, "TA": 2, "TD": 2, "GRBM": 2}
+DERIVED_SLOTS = {"FETCH_SIZE": {"TCC": 3}, "WRITE_SIZE": {"TCC": 2}}
+
+# Kernels of the headline workloads, by template signature.
+KERNELS = {
+    "prefill": "attn::prefill_kernel<1, 128, false, 8, 1>",
+    "decode_split": "attn::decode_split_kernel<0, 64, 1>",
+    "decode_merge": "attn::decode_merge_kernel<0, 64>",
+    "gqa_split": "attn::decode_split_mfma_kernel<1, 128>",
+    "gqa_merge": "attn::decode_merge_kernel<1, 128>",
+    "bwd_delta": "attn::bwd_delta_kernel<1, 128>",
+    "bwd_dq": "attn::bwd_dq_kernel<1, 128, false, 8>",
+    "bwd_dkdv": "attn::bwd_dkdv_kernel<1, 128, false>",
+}
+# Prefill sources whose hash keys the stored traffic figure (the same files bench.py hashes).
+PREFILL_SOURCES = ["exact_attention_prefill_amd/csrc/prefill.hip", "exact_attention_prefill_amd/csrc/attn_device.h"]
+
+
+def check_counter_set(counters):
+    """Raise ValueError if a set needs more slots of a block than one pass has."""
+    used = {}
+    for c in counters:
+        for blk, n in DERIVED_SLOTS.get(c, {c.split("_", 1)[0]: 1}).items():
+            used[blk] = used.get(blk, 0) + n
+    for blk, n in used.items():
+        if n > BLOCK_SLOTS.get(blk, 0):
+            raise ValueError(f"counter set {counters} needs {n} {blk} slots, one pass has {BLOCK_SLOTS.get(blk, 0)}")
+
+
+def bench_args(trace: bool):
+    if trace:
+        return ["--steps", str(TRACE_STEPS), "--warmup", str(TRACE_WARMUP), "--no-cpu-baseline", "--decode-iters",
+                str(TRACE_DECODE_ITERS), "--no-head-sizes", "--no-configs"]
+    return ["--steps", str(PMC_STEPS), "--warmup", str(PMC_WARMUP), "--no-cpu-baseline", "--decode-iters",
+            str(PMC_DECODE_ITERS), "--bwd-iters", "2", "--no-head-sizes", "--no-configs", "--calibrate-copy",
+            str(CALIBRATE_MIB)]
+
+
+def pass_command(name: str, out: str, python: str = sys.executable):
+    """The command line of one pass (a list for subprocess; the program directly after --)."""
+    d = os.path.join(out, name)
+    if name == "trace":
+        prof = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", d, "-o", "run"]
+        limit = ["timeout", "-k", "10", "300"]
+    else:
+        counters = COUNTER_SETS[name]
+        check_counter_set(counters)
+        prof = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "run"]
+        limit = ["timeout", "-s", "KILL", "120"]
+    return limit + prof + ["--", python, "-u", "bench.py", *bench_args(name == "trace")]
+
+
+def run_passes(out: str, passes):
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name in passes:
+        cmd = pass_command(name, out)
+        print(f"[evidence] pass {name}: {' '.join(cmd)}", flush=True)
+        with open(os.path.join(out, f"{name}.log"), "w") as log:
+            r = subprocess.run(cmd, cwd=ROOT, env=env, stdout=log, stderr=subprocess.STDOUT)
+        print(f"[evidence] pass {name} exit {r.returncode}", flush=True)
+        if r.returncode != 0:
+            return False
+    return True
+
+
+# ---- reading rocprofv3 CSV files ----
+
+def _find(out: str, name: str, suffix: str):
+    d = os.path.join(out, name)
+    if not os.path.isdir(d):
+        return None
+    for root, _dirs, files in os.walk(d):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def read_agent(path):
+    """(CUs, SIMDs per CU, XCDs, peak MHz) of the first GPU agent."""
+    for r in csv.DictReader(open(path)):
+        if r.get("Agent_Type") == "GPU":
+            return (int(r["Cu_Count"]), int(r["Simd_Per_Cu"]), int(r["Num_Xcc"]), float(r["Max_Engine_Clk_Fcompute"]))
+    raise ValueError(f"no GPU agent in {path}")
+
+
+def read_trace(path):
+    """Kernel dispatches in order: [(name, duration ns)]."""
+    rows = [r for r in csv.DictReader(open(path)) if r.get("Kind", "KERNEL_DISPATCH") == "KERNEL_DISPATCH"]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows]
+
+
+def read_counters(path):
+    """Dispatches in order: [(name, duration ns, {counter: value})], values summed over
+    the rows rocprofv3 writes for one dispatch and counter."""
+    by = {}
+    for r in csv.DictReader(open(path)):
+        key = int(r["Dispatch_Id"])
+        e = by.setdefault(key, [r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}])
+        e[2][r["Counter_Name"]] = e[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [tuple(by[k]) for k in sorted(by)]
+
+
+def select(dispatches, signature, start=0, count=None):
+    """Dispatches whose kernel name contains the signature, in order, sliced."""
+    got = [d for d in dispatches if signature in d[0]]
+    return got[start:] if count is None else got[start:start + count]
+
+
+def calibration(dispatches, counter, true_kib):
+    """true / measured KiB for the largest plain device copy (the calibration copy)."""
+    vals = [d[2][counter] for d in dispatches if "copyBuffer" in d[0] and counter in d[2]]
+    if not vals or max(vals) <= 0:
+        return None
+    return true_kib / max(vals)
+
+
+def median_counter(dispatches, counter):
+    vals = [d[2][counter] for d in dispatches if counter in d[2]]
+    return statistics.median(vals) if vals else None
+
+
+def mfma_utilisation(busy_cycles, grbm_active, n_simd, n_xcd):
+    """Fraction of SIMD cycles with the matrix core busy; cycles are GRBM_GUI_ACTIVE per XCD."""
+    cycles = grbm_active / n_xcd
+    return busy_cycles / (n_simd * cycles)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bench_record(log_path):
+    """The JSON line bench.py printed in a pass, or None."""
+    if not os.path.exists(log_path):
+        return None
+    for line in open(log_path):
+        if line.startswith("{"):
+            return json.loads(line)
+    return None
+
+
+def summarize(out: str):
+    """Write summary.md and prefill_headline_counters.json from the passes present."""
+    tr_path = _find(out, "trace", "kernel_trace.csv")
+    agent_path = _find(out, "trace", "agent_info.csv") or next(
+        (p for p in (_find(out, n, "agent_info.csv") for n in COUNTER_SETS) if p), None)
+    if agent_path is None:
+        raise FileNotFoundError(f"no rocprofv3 output under {out}")
+    cus, simd_per_cu, n_xcd, peak_mhz = read_agent(agent_path)
+    n_simd = cus * simd_per_cu
+    rec = bench_record(os.path.join(out, "trace.log"))
+    trace = read_trace(tr_path) if tr_path else []
+    pmc = {}
+    for name in COUNTER_SETS:
+        p = _find(out, name, "counter_collection.csv")
+        if p:
+            pmc[name] = read_counters(p)
+
+    n_pre_trace = TRACE_WARMUP + TRACE_STEPS
+    n_pre_pmc = PMC_WARMUP + PMC_STEPS
+
+    def kernel_slices(key, dispatches, n_plain):
+        sig = KERNELS[key]
+        if key == "prefill":  # the step's launches come first; later ones carry the lse output
+            return select(dispatches, sig, 0, n_plain)
+        if key in ("decode_split", "decode_merge"):  # cold calls follow the step's
+            return select(dispatches, sig, n_plain)
+        return select(dispatches, sig)
+
+    fc = calibration(pmc.get("fetch", []), "FETCH_SIZE", CALIBRATE_MIB * 1024)
+    wc = calibration(pmc.get("write", []), "WRITE_SIZE", CALIBRATE_MIB * 1024)
+    rows = {}
+    for key in KERNELS:
+        t = kernel_slices(key, trace, n_pre_trace)
+        r = {"dispatches": len(t), "avg_us": statistics.mean(d[1] for d in t) / 1e3 if t else None,
+             "min_us": min(d[1] for d in t) / 1e3 if t else None}
+        f = median_counter(kernel_slices(key, pmc.get("fetch", []), n_pre_pmc), "FETCH_SIZE")
+        w = median_counter(kernel_slices(key, pmc.get("write", []), n_pre_pmc), "WRITE_SIZE")
+        if f is not None and w is not None and fc and wc:
+            r["fetch_kib_raw"], r["write_kib_raw"] = f, w
+            r["hbm_bytes"] = f * fc * 1024 + w * wc * 1024
+        m = kernel_slices(key, pmc.get("mfma", []), n_pre_pmc)
+        busy = median_counter(m, "SQ_VALU_MFMA_BUSY_CYCLES")
+        grbm = median_counter(m, "GRBM_GUI_ACTIVE")
+        insts = median_counter(m, "SQ_INSTS_MFMA")
+        if busy is not None and grbm:
+            r["mfma_busy"] = mfma_utilisation(busy, grbm, n_simd, n_xcd)
+            r["mfma_insts"] = insts
+            r["mfma_busy_from_insts"] = insts * MFMA_CYCLES / (n_simd * grbm / n_xcd) if insts is not None else None
+            dur = statistics.median(d[1] for d in m)
+            # GRBM_GUI_ACTIVE also counts the cycles around a dispatch, so the clock is
+            # only meaningful for dispatches far longer than that margin.
+            r["clock_ghz"] = (grbm / n_xcd) / dur if dur >= MIN_CLOCK_NS else None
+            co = median_counter(m, "SQ_VALU_MFMA_COEXEC_CYCLES")
+            r["coexec"] = co / (n_simd * grbm / n_xcd) if co is not None else None
+        lds = kernel_slices(key, pmc.get("lds", []), n_pre_pmc)
+        bank, active = median_counter(lds, "SQ_LDS_BANK_CONFLICT"), median_counter(lds, "SQ_LDS_IDX_ACTIVE")
+        if bank is not None and active:
+            r["lds_conflict_frac"] = bank / active
+        rows[key] = r
+
+    pre = rec["config"]["prefill"] if rec else {"B": 1, "H": 16, "N": 16384, "d": 128, "causal": False}
+    flop = 4.0 * pre["B"] * pre["H"] * pre["N"] * pre["N"] * pre["d"] / (2 if pre["causal"] else 1)
+    dec_bytes = rec["decode"]["bytes"] if rec else None
+    p = rows["prefill"]
+    pre_tf = flop / (p["avg_us"] * 1e-6) / 1e12 if p.get("avg_us") else None
+    ds, dm = rows["decode_split"], rows["decode_merge"]
+    dec_us = ds["avg_us"] + dm["avg_us"] if ds.get("avg_us") and dm.get("avg_us") else None
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9 if dec_us and dec_bytes else None
+    alg_pre_bytes = 4 * pre["B"] * pre["H"] * pre["N"] * pre["d"] * 2
+    sha = source_hash(PREFILL_SOURCES)
+    derived = {
+        "prefill_tflops": pre_tf, "prefill_frac": pre_tf / PEAK_BF16_TFLOPS if pre_tf else None,
+        "prefill_mfma_busy": p.get("mfma_busy"), "prefill_clock_ghz": p.get("clock_ghz"),
+        "prefill_mfma_insts": p.get("mfma_insts"), "prefill_mfma_insts_algorithmic": flop / (32 * 32 * 16 * 2),
+        "prefill_hbm_bytes": p.get("hbm_bytes"), "prefill_algorithmic_bytes": alg_pre_bytes,
+        "decode_us_split_plus_merge": dec_us, "decode_gbs": dec_gbs,
+        "decode_frac": dec_gbs / PEAK_HBM_GBS if dec_gbs else None, "decode_algorithmic_bytes": dec_bytes,
+        "decode_split_hbm_bytes": ds.get("hbm_bytes"),
+    }
+    with open(os.path.join(out, "summary.json"), "w") as f:
+        json.dump({"agent": {"cus": cus, "simd_per_cu": simd_per_cu, "xcds": n_xcd, "peak_mhz": peak_mhz},
+                   "calibration": {"fetch": fc, "write": wc}, "kernels": rows, "derived": derived,
+                   "prefill_sha": sha}, f, indent=1)
+    if p.get("hbm_bytes") is not None:
+        with open(os.path.join(out, "prefill_headline_counters.json"), "w") as f:
+            json.dump({"kernel": "void " + KERNELS["prefill"] + "(attn::PrefillParams)",
+                       "workload": "prefill B=1 H=16 N=16384 d=128 bf16 non-causal", "kernel_sha": sha,
+                       "kernel_sources": PREFILL_SOURCES, "fetch_size_kib_per_dispatch": p["fetch_kib_raw"],
+                       "write_size_kib_per_dispatch": p["write_kib_raw"], "fetch_calibration": fc,
+                       "write_calibration": wc, "calibration_copy_kib": CALIBRATE_MIB * 1024,
+                       "hbm_bytes_per_launch": round(p["hbm_bytes"]), "algorithmic_bytes_per_launch": alg_pre_bytes},
+                      f, indent=1)
+            f.write("\n")
+    with open(os.path.join(out, "summary.md"), "w") as f:
+        f.write(render(out, rows, derived, (cus, simd_per_cu, n_xcd, peak_mhz), fc, wc, sha))
+    return derived
+
+
+def _fmt(x, spec):
+    return "-" if x is None else format(x, spec)
+
+
+def render(out, rows, derived, agent, fc, wc, sha):
+    cus, spc, nx, mhz = agent
+    rel = os.path.relpath(out, ROOT)
+    lines = ["# rocprofv3 evidence: headline prefill, ragged decode, grouped decode, backward", "",
+             f"Made by `python -m exact_attention_prefill_amd.evidence --out {rel}`, which ran, from the",
+             f"repository root with TMPDIR=/tmp, one command per pass (`<out>` = `{rel}`):", "", "```"]
+    for name in ALL_PASSES:
+        if os.path.exists(os.path.join(out, f"{name}.log")):
+            cmd = pass_command(name, "<out>", python="python3")
+            lines.append(" ".join(cmd))
+    lines += ["```", "",
+              f"GPU: {cus} CUs x {spc} SIMDs in {nx} XCDs, peak clock {mhz:.0f} MHz. Prefill sources "
+              f"(prefill.hip + attn_device.h) sha256[:16] `{sha}`; decode.hip "
+              f"`{source_hash(['exact_attention_prefill_amd/csrc/decode.hip'])}`; bwd.hip "
+              f"`{source_hash(['exact_attention_prefill_amd/csrc/bwd.hip'])}`.", "",
+              f"HBM calibration (a plain {CALIBRATE_MIB} MiB device copy in the same process): FETCH_SIZE x "
+              f"{_fmt(fc, '.4f')}, WRITE_SIZE x {_fmt(wc, '.4f')}.", "",
+              "| kernel | dispatches | avg us | min us | HBM MB (cal.) | MFMA busy | by MFMA count | "
+              "VALU+MFMA both busy | clock GHz | LDS conflict cycles |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for key, r in rows.items():
+        hbm = r.get("hbm_bytes")
+        lines.append(
+            f"| `{KERNELS[key]}` | {r['dispatches']} | {_fmt(r['avg_us'], '.2f')} | {_fmt(r['min_us'], '.2f')} | "
+            f"{_fmt(hbm / 1e6 if hbm is not None else None, '.2f')} | {_fmt(r.get('mfma_busy'), '.1%')} | "
+            f"{_fmt(r.get('mfma_busy_from_insts'), '.1%')} | {_fmt(r.get('coexec'), '.1%')} | "
+            f"{_fmt(r.get('clock_ghz'), '.2f')} | {_fmt(r.get('lds_conflict_frac'), '.1%')} |")
+    d = derived
+    hb, ab = d["prefill_hbm_bytes"], d["prefill_algorithmic_bytes"]
+    lines += ["",
+              "Prefill rows are the step's launches (warm-ups and timed steps), before the launches that also",
+              "write the log-sum-exp; decode rows are the cold calls (a 512 MiB read before each).", "",
+              "## Derived", "",
+              f"- prefill: {_fmt(d['prefill_tflops'], '.1f')} TFLOP/s = {_fmt(d['prefill_frac'], '.1%')} of "
+              f"{PEAK_BF16_TFLOPS:.0f} TFLOP/s (trace average); MFMA busy {_fmt(d['prefill_mfma_busy'], '.1%')} at "
+              f"{_fmt(d['prefill_clock_ghz'], '.2f')} GHz; MFMA instructions {_fmt(d['prefill_mfma_insts'], '.4g')} vs "
+              f"{d['prefill_mfma_insts_algorithmic']:.4g} for the algorithmic flop",
+              f"- prefill HBM: {_fmt(hb / 1e6 if hb else None, '.1f')} MB per launch vs {ab / 1e6:.1f} MB algorithmic "
+              f"(Q, K, V in, O out): {_fmt(hb / ab if hb else None, '.2f')}x",
+              f"- decode: split + merge {_fmt(d['decode_us_split_plus_merge'], '.2f')} us (kernel time) = "
+              f"{_fmt(d['decode_gbs'], '.0f')} GB/s = {_fmt(d['decode_frac'], '.1%')} of {PEAK_HBM_GBS:.0f} GB/s for "
+              f"{_fmt(d['decode_algorithmic_bytes'], 'd')} algorithmic bytes; split HBM "
+              f"{_fmt(d['decode_split_hbm_bytes'] / 1e6 if d['decode_split_hbm_bytes'] else None, '.2f')} MB", ""]
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--out", required=True, help="output folder for the rocprofv3 files and the summary")
+    ap.add_argument("--passes", default=",".join(ALL_PASSES))
+    ap.add_argument("--summarize-only", action="store_true")
+    a = ap.parse_args(argv)
+    out = os.path.abspath(a.out)
+    os.makedirs(out, exist_ok=True)
+    passes = [p for p in a.passes.split(",") if p]
+    for p in passes:
+        if p not in ALL_PASSES:
+            raise SystemExit(f"unknown pass {p!r}; passes: {', '.join(ALL_PASSES)}")
+        if p != "trace":
+            check_counter_set(COUNTER_SETS[p])
+    ok = True if a.summarize_only else run_passes(out, passes)
+    d = summarize(out)
+    print(json.dumps({k: v for k, v in d.items() if v is not None}), flush=True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,145 @@
+"""Host logic of the rocprofv3 evidence harness, on synthetic rocprofv3 CSV files.
+
+No GPU and no profiler: the files below stand in for what rocprofv3 writes, with
+values chosen so every derived figure has a known answer.
+"""
+
+import csv
+import json
+import os
+
+import pytest
+
+from exact_attention_prefill_amd import evidence as ev
+
+PRE = ev.KERNELS["prefill"]
+SPLIT = ev.KERNELS["decode_split"]
+MERGE = ev.KERNELS["decode_merge"]
+
+
+def test_every_counter_set_fits_one_pass():
+    for name, counters in ev.COUNTER_SETS.items():
+        ev.check_counter_set(counters)  # raises if not
+
+
+def test_oversized_sets_are_refused():
+    with pytest.raises(ValueError):
+        ev.check_counter_set([f"SQ_X{i}" for i in range(9)])
+    with pytest.raises(ValueError):  # FETCH_SIZE takes 3 TCC slots, WRITE_SIZE 2: 5 > 4
+        ev.check_counter_set(["FETCH_SIZE", "WRITE_SIZE"])
+    with pytest.raises(ValueError):
+        ev.check_counter_set(["GRBM_GUI_ACTIVE", "GRBM_COUNT", "GRBM_X"])
+
+
+def test_commands_put_the_program_right_after_the_separator():
+    for name in ev.ALL_PASSES:
+        cmd = ev.pass_command(name, "/tmp/o", python="/usr/bin/python3")
+        i = cmd.index("--")
+        assert cmd[i + 1] == "/usr/bin/python3" and cmd[i + 2:i + 4] == ["-u", "bench.py"]
+        assert cmd[0] == "timeout" and "rocprofv3" in cmd
+        if name == "trace":
+            assert "--kernel-trace" in cmd and "--pmc" not in cmd
+        else:
+            assert cmd[1:3] == ["-s", "KILL"] and "--kernel-trace" not in cmd and "--calibrate-copy" in cmd
+            assert not {"-s", "--sys-trace", "-r", "--runtime-trace"} & set(cmd[cmd.index("rocprofv3"):i])
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _agent(path):
+    _write(path, ["Agent_Type", "Cu_Count", "Simd_Per_Cu", "Num_Xcc", "Max_Engine_Clk_Fcompute"],
+           [["CPU", 16, 0, 1, 0], ["GPU", 2, 4, 2, 2400]])
+
+
+def _trace(path, seq):
+    rows, t = [], 1000
+    for name, dur in seq:
+        rows.append(["KERNEL_DISPATCH", name, t, t + dur])
+        t += dur + 10
+    _write(path, ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+
+
+def _pmc(path, seq):
+    """seq: (name, duration ns, {counter: value}); one row per counter per dispatch."""
+    rows, t = [], 1000
+    for i, (name, dur, vals) in enumerate(seq):
+        for c, v in vals.items():
+            rows.append([i + 1, name, c, v, t, t + dur])
+        t += dur + 10
+    _write(path, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                  "End_Timestamp"], rows)
+
+
+@pytest.fixture
+def run_dir(tmp_path):
+    out = str(tmp_path)
+    _agent(os.path.join(out, "trace", "h", "run_agent_info.csv"))
+    n_pre = ev.TRACE_WARMUP + ev.TRACE_STEPS
+    seq = []
+    for _ in range(n_pre):  # the step: prefill then decode (warm)
+        seq += [(PRE, 2_000_000), (SPLIT, 999_999), (MERGE, 999_999)]
+    seq += [(SPLIT, 15_000), (MERGE, 5_000)] * ev.TRACE_DECODE_ITERS  # cold decode
+    seq += [(PRE, 9_000_000)] * 3  # later launches with the lse output: not the step's
+    _trace(os.path.join(out, "trace", "h", "run_kernel_trace.csv"), seq)
+    rec = {"config": {"prefill": {"B": 1, "H": 16, "N": 16384, "d": 128, "causal": False}},
+           "decode": {"bytes": 64_000_000}}
+    with open(os.path.join(out, "trace.log"), "w") as f:
+        f.write("[bench] noise\n" + json.dumps(rec) + "\n")
+    n_pmc = ev.PMC_WARMUP + ev.PMC_STEPS
+    cal = ev.CALIBRATE_MIB * 1024
+
+    def pmc_seq(counter, pre_val, split_val, copy_val):
+        s = [("__amd_rocclr_copyBuffer", 100, {counter: 3.0})]
+        for _ in range(n_pmc):
+            s += [(PRE, 1_000_000, {counter: pre_val}), (SPLIT, 1, {counter: 1e9}), (MERGE, 1, {counter: 1e9})]
+        s += [(SPLIT, 1, {counter: split_val}), (MERGE, 1, {counter: 0.0})] * ev.PMC_DECODE_ITERS
+        s += [(PRE, 1_000_000, {counter: 1e12})]  # an lse launch: excluded
+        s += [("__amd_rocclr_copyBuffer", 100, {counter: copy_val})] * 3
+        return s
+
+    _pmc(os.path.join(out, "fetch", "h", "run_counter_collection.csv"), pmc_seq("FETCH_SIZE", 1000.0, 500.0, cal / 2))
+    _pmc(os.path.join(out, "write", "h", "run_counter_collection.csv"), pmc_seq("WRITE_SIZE", 300.0, 2.0, cal))
+    # MFMA pass: GRBM_GUI_ACTIVE summed over 2 XCDs = 1.5e6 cycles each over a 1 ms dispatch
+    # (1.5 GHz); 8 SIMDs busy 6e6 cycles in all = 50%; 1.875e5 MFMAs x 32 cycles / (8 x 1.5e6) = 50%;
+    # both units busy 1.2e6 cycles = 10%.
+    mf = [(PRE, 1_000_000, {"GRBM_GUI_ACTIVE": 3.0e6, "SQ_VALU_MFMA_BUSY_CYCLES": 6.0e6, "SQ_INSTS_MFMA": 1.875e5,
+                            "SQ_VALU_MFMA_COEXEC_CYCLES": 1.2e6})] * n_pmc
+    _pmc(os.path.join(out, "mfma", "h", "run_counter_collection.csv"), mf)
+    return out
+
+
+def test_summary_derivations(run_dir):
+    d = ev.summarize(run_dir)
+    flop = 4.0 * 16 * 16384 * 16384 * 128
+    assert d["prefill_tflops"] == pytest.approx(flop / 2e-3 / 1e12)  # the 2 ms step launches only
+    assert d["prefill_frac"] == pytest.approx(d["prefill_tflops"] / 2500)
+    assert d["decode_us_split_plus_merge"] == pytest.approx(20.0)  # cold calls only
+    assert d["decode_gbs"] == pytest.approx(64e6 / 20e-6 / 1e9)
+    # FETCH factor 2 (copy read half), WRITE factor 1
+    assert d["prefill_hbm_bytes"] == pytest.approx((1000.0 * 2 + 300.0) * 1024)
+    assert d["decode_split_hbm_bytes"] == pytest.approx((500.0 * 2 + 2.0) * 1024)
+    assert d["prefill_mfma_busy"] == pytest.approx(0.5)
+    assert d["prefill_clock_ghz"] == pytest.approx(1.5)
+    s = json.load(open(os.path.join(run_dir, "summary.json")))
+    assert s["kernels"]["prefill"]["mfma_busy_from_insts"] == pytest.approx(0.5)
+    assert s["kernels"]["prefill"]["coexec"] == pytest.approx(0.1)
+    assert s["calibration"] == {"fetch": pytest.approx(2.0), "write": pytest.approx(1.0)}
+    c = json.load(open(os.path.join(run_dir, "prefill_headline_counters.json")))
+    assert c["kernel_sha"] == ev.source_hash(ev.PREFILL_SOURCES)
+    assert c["hbm_bytes_per_launch"] == round((1000.0 * 2 + 300.0) * 1024)
+    assert c["algorithmic_bytes_per_launch"] == 4 * 16 * 16384 * 128 * 2
+    md = open(os.path.join(run_dir, "summary.md")).read()
+    assert "python3 -u bench.py" in md and PRE in md
+
+
+def test_stored_traffic_key_matches_what_bench_hashes():
+    import bench
+
+    assert [os.path.relpath(p, ev.ROOT) for p in bench.KERNEL_SOURCES] == ev.PREFILL_SOURCES
+    assert bench.kernel_hash() == ev.source_hash(ev.PREFILL_SOURCES)
