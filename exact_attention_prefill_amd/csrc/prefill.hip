@@ -58,17 +58,19 @@ struct PrefillParams {
   float* lse;     // optional [B][H][N] row log-sum-exp (natural log), or null
 };
 
-// Two waves per SIMD need <= 256 registers a wave: QB = 1 up to d = 128.
+// Two waves per SIMD need <= 256 registers a wave: QB = 1 up to d = 128, and QB = 2
+// at d = 64 (246 registers).
 template <int D, int QB>
 constexpr int prefill_waves_per_simd() {
-  return (QB == 1 && D <= 128) ? 2 : 1;
+  return ((QB == 1 && D <= 128) || (QB == 2 && D == 64)) ? 2 : 1;
 }
 
 // NW waves per workgroup, each owning QB blocks of 32 query rows.  QB = 1: two waves
 // share each SIMD (<= 256 registers) up to d = 128; d = 256 runs one wave per SIMD.
 // QB = 2: the two row blocks share every K and V operand read, halving LDS traffic
-// per MFMA; a wave then needs ~350 registers, so one wave runs per SIMD with the MFMA
-// accumulators in AGPRs.
+// per MFMA and giving each wave two independent softmax chains.  At d = 64 a wave of
+// two blocks still fits two per SIMD; at d = 128 it needs ~350 registers, one wave
+// per SIMD with the MFMA accumulators in AGPRs.
 template <int DT, int D, bool CAUSAL, int NW, int QB>
 __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
@@ -295,10 +297,12 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   //   VALU:         P_{u+1} = 2^(c S_{u+1} - m).
   // P_{u+1} is computed optimistically with the current m.  Every p of a lane is at
   // most the lane's sum of the unit, so a sum within kSumGuard means no p left the
-  // safe range and m may stay; otherwise the real row max decides: rows whose max
-  // exceeds m by more than 2^8 raise m (alpha = 1 exactly elsewhere, so each row
-  // depends on its own scores alone), P_{u+1} is recomputed and l and O rescaled (O
-  // after this iteration's MFMAs into it).  The softmax is spread over all the
+  // safe range and m may stay; otherwise the real row max decides: a row whose own
+  // guard fired (in either half of its keys) and whose max exceeds m by more than 2^8
+  // raises m, P_{u+1} is recomputed and l and O rescaled (O after this iteration's
+  // MFMAs into it).  Every other row of the wave keeps m with alpha = 1 exactly and
+  // recomputes the same P, so a row's result depends on its own scores alone, never on
+  // which rows share its wave.  The softmax is spread over all the
   // iteration's MFMAs, about three VALU instructions (one exponential) per MFMA, with
   // each dependent step in a later slot than its input.
   // scur = S_{u+1} (scored last iteration), snext receives S_{u+2}; pcur = P_u,
@@ -377,8 +381,9 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
       for (int cb = 0; cb < QB; ++cb) {
+        const bool row_over = xhalf_max(l_unit[cb]) > kSumGuard;  // this row's own guard
         const float cand = unit_max(scur[cb]) * p.c;
-        const bool raise = cand > m_run[cb] + kLazyLog2;
+        const bool raise = row_over && cand > m_run[cb] + kLazyLog2;
         const float alpha = raise ? fast_exp2(m_run[cb] - cand) : 1.f;
         m_run[cb] = raise ? cand : m_run[cb];
         neg_m[cb] = -m_run[cb];
@@ -490,8 +495,11 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   // four-wave form (128 rows, two workgroups per CU), halving L2-to-LDS traffic per
   // MFMA; it pays (+2-3% at d = 128, 16K tokens) when the grid still gives every CU
   // at least four such workgroups, and small grids keep the finer four-wave blocks.
-  // The 64-row form (QB = 2) halves LDS operand reads per MFMA but, at one wave per
-  // SIMD, measured 5-8% slower, so it is not selected.
+  // The 64-row form (QB = 2) halves LDS operand reads per MFMA.  At d = 128 it runs
+  // one wave per SIMD and measured 5-8% slower, so it is not selected there; at d = 64
+  // it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
+  // eight-wave grids, which then take 512-row workgroups.  d = 32 measured 5-6% slower
+  // with it and keeps one block per wave.
   // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
   // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
   // workgroup per CU.
@@ -499,7 +507,10 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
     const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-    if (blocks8 >= 4LL * num_cus) return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
+    if (blocks8 >= 4LL * num_cus) {
+      if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
+      else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
+    }
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }
 }

@@ -1,0 +1,123 @@
+"""d = 64 prefill on large grids: two 32-row blocks per wave.
+
+Grids of at least four 256-row blocks per CU (256 CUs: B*H*ceil(N/256) >= 1024) run
+d = 64 with eight-wave, 512-row workgroups in which every wave owns two 32-row blocks
+and reads each K and V operand once for both.  The shapes below reach that form with
+ragged lengths; smaller grids (one head at a time) run one block per wave.  A row's
+arithmetic does not depend on the workgroup form, so every row of the large call must
+equal the one-head call bit for bit; sampled rows are also checked against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_prefill_amd as ea
+import oracle
+import workloads as W
+from parity import check, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+TWO_BLOCK = [
+    W.PrefillCase("prefill_b1_h64_n4001_d64_bf16_full", 1, 64, 4001, 64, "bf16", False, 0.125),
+    W.PrefillCase("prefill_b1_h64_n4001_d64_bf16_causal", 1, 64, 4001, 64, "bf16", True, 0.125),
+    W.PrefillCase("prefill_b4_h16_n3969_d64_f16_causal", 4, 16, 3969, 64, "f16", True, 0.125),
+    W.PrefillCase("prefill_b4_h16_n3969_d64_f16_full", 4, 16, 3969, 64, "f16", False, -0.2),
+]
+
+
+def reaches_two_block_form(case):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return case.B * case.H * -(-case.N // 256) >= 4 * cus
+
+
+def one_head(q, k, v, b, h, causal, scale, lse=False):
+    sl = lambda t: t[b:b + 1, h:h + 1].contiguous()  # noqa: E731
+    return ea.prefill(sl(q), sl(k), sl(v), causal=causal, scale=scale, lse=lse)
+
+
+def grow_keys(k, N):
+    growth = (1.0 + 6.0 * torch.arange(N, dtype=torch.float32) / N).view(1, 1, N, 1)
+    return (k.float() * growth).to(k.dtype)
+
+
+@pytest.mark.parametrize("case", TWO_BLOCK, ids=lambda c: c.name)
+def test_two_block_rows_match_one_head_and_oracle(case):
+    assert reaches_two_block_form(case)
+    q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=7)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ea.prefill(qd, kd, vd, causal=case.causal, scale=case.scale)
+    torch.cuda.synchronize()
+    rows = W.prefill_rows_sample(case.N, 40, seed=7)
+    for b, h in ((0, 0), (case.B - 1, case.H - 1), (case.B // 2, 5)):
+        single = one_head(qd, kd, vd, b, h, case.causal, case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out[b, h].view(torch.int16), single[0, 0].view(torch.int16)), (case.name, b, h)
+        ref = oracle.prefill_rows(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]), f64(v[b:b + 1, h:h + 1]),
+                                  case.causal, case.scale, 0, 0, rows)
+        check(f64(out[b, h, rows]), ref, case.dtype, f"{case.name} b={b} h={h}")
+    assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_block_growing_scores(causal):
+    """Keys growing along the sequence push the row maxima up past the optimistic
+    margin again and again, so the redo path runs with both blocks of a wave live."""
+    case = TWO_BLOCK[0]
+    q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=21)
+    k = grow_keys(k, case.N)
+    scale = 2.0 / np.sqrt(case.d)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = W.prefill_rows_sample(case.N, 40, seed=21)
+    for h in (0, 33, 63):
+        single = one_head(qd, kd, vd, 0, h, causal, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0, h].view(torch.int16), single[0, 0].view(torch.int16)), h
+        ref = oracle.prefill_rows(f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1]), causal, scale, 0, 0,
+                                  rows)
+        check(f64(out[0, h, rows]), ref, case.dtype, f"growing scores two-block h={h} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_block_grouped_heads(causal):
+    """64 query heads over 8 K/V heads at d = 64: each query head reads its group's
+    K/V head; rows must equal the multi-head call on repeated K/V heads."""
+    B, Hq, Hkv, N, d = 1, 64, 8, 4000, 64
+    scale = 0.125
+    q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=5)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
+    g = Hq // Hkv
+    rep = ea.prefill(qd, kd.repeat_interleave(g, dim=1).contiguous(), vd.repeat_interleave(g, dim=1).contiguous(),
+                     causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), rep.view(torch.int16))
+    rows = W.prefill_rows_sample(N, 32, seed=5)
+    for h in (0, 7, 8, 63):
+        ref = oracle.prefill_rows(f64(q), f64(k), f64(v), causal, scale, 0, h, rows)
+        check(f64(out[0, h, rows]), ref, "bf16", f"two-block gqa h={h} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_block_lse(causal):
+    """The row log-sum-exp output of the two-block form: against the oracle on sampled
+    rows, equal to the one-head call, and the output unchanged by asking for it."""
+    case = TWO_BLOCK[0]
+    q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=9)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=case.scale, lse=True)
+    plain = ea.prefill(qd, kd, vd, causal=causal, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    rows = W.prefill_rows_sample(case.N, 40, seed=9)
+    for h in (0, 63):
+        _, single = one_head(qd, kd, vd, 0, h, causal, case.scale, lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(lse[0, h], single[0, 0]), h
+        ref = oracle.prefill_lse_rows(f64(q), f64(k), causal, case.scale, 0, h, rows)
+        err = float(np.max(np.abs(lse[0, h, rows].double().cpu().numpy() - ref)))
+        assert err <= 4.5e-3, f"two-block lse h={h}: {err:.3e}"
