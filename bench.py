@@ -29,7 +29,9 @@ prefill (B=1, H=1, N=128, d=64, fp16), the GPT-2-like prompt (B=1, H=12, N=2048,
 fp16, full and causal), the dense d=128 token splits (B*N = 16384 at H=16), the long
 sequences (B=1, H=24, d=128, bf16: N=32768 full, N=16384 causal) and the batch-1
 decode over a full 4096-row cache, cold like the step's decode.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill; in
+the same host leg the oracle checks this run's outputs on sampled rows (`parity`).
+With --no-cpu-baseline the oracle is not imported at all and both are null.
 """
 
 from __future__ import annotations
@@ -341,26 +343,32 @@ def main():
         del eq, ek, ev_, eout, ews
         log("configs: " + ", ".join(f"{k} {v.get('tflops', v.get('gbs'))}" for k, v in configs.items()))
 
-    # Parity spot check of this run's outputs against the oracle (sampled rows).
-    import oracle
+    # The host leg: the fp64 CPU oracle, run only with the CPU baseline (it is skipped
+    # with --no-cpu-baseline, as in every profiled run).  It checks this run's outputs
+    # on sampled rows and then times the oracle itself.
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
 
-    rows = W.prefill_rows_sample(P.N, 16, 0)
-    perr = 0.0
-    for h in (0, P.H - 1):
-        f = lambda t: t[0, h].to(torch.float64).numpy()[None, None]  # noqa: E731
-        ref = oracle.prefill_rows(f(qc), f(kc), f(vc), P.causal, P.scale, 0, 0, rows)
-        got = out[0, h, rows].to(torch.float64).cpu().numpy()
-        perr = max(perr, float(np.max(np.abs(got - ref))))
-    dref = oracle.decode(dq.double().numpy(), dk.double().numpy(), dv.double().numpy(), dl.numpy(), D.scale)
-    derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
-    gref = oracle.decode(gq.double().numpy(), gk.double().numpy(), gv.double().numpy(), gl.numpy(), GQ.scale)
-    gerr = float(np.max(np.abs(gout.double().cpu().numpy() - gref)))
-    bdq_rows = oracle.backward_dq_rows(qc[:, :1].double().numpy(), kc[:, :1].double().numpy(),
-                                       vc[:, :1].double().numpy(), bdo[:, :1].double().cpu().numpy(),
-                                       P.causal, P.scale, 0, 0, rows)
-    berr = float(np.max(np.abs(bgrads[0][0, 0, rows].double().cpu().numpy() - bdq_rows)))
-    log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}, grouped decode {gerr:.2e}, "
-        f"backward dq sampled {berr:.2e}")
+        rows = W.prefill_rows_sample(P.N, 16, 0)
+        perr = 0.0
+        for h in (0, P.H - 1):
+            f = lambda t: t[0, h].to(torch.float64).numpy()[None, None]  # noqa: E731
+            ref = oracle.prefill_rows(f(qc), f(kc), f(vc), P.causal, P.scale, 0, 0, rows)
+            got = out[0, h, rows].to(torch.float64).cpu().numpy()
+            perr = max(perr, float(np.max(np.abs(got - ref))))
+        dref = oracle.decode(dq.double().numpy(), dk.double().numpy(), dv.double().numpy(), dl.numpy(), D.scale)
+        derr = float(np.max(np.abs(dout.double().cpu().numpy() - dref)))
+        gref = oracle.decode(gq.double().numpy(), gk.double().numpy(), gv.double().numpy(), gl.numpy(), GQ.scale)
+        gerr = float(np.max(np.abs(gout.double().cpu().numpy() - gref)))
+        bdq_rows = oracle.backward_dq_rows(qc[:, :1].double().numpy(), kc[:, :1].double().numpy(),
+                                           vc[:, :1].double().numpy(), bdo[:, :1].double().cpu().numpy(),
+                                           P.causal, P.scale, 0, 0, rows)
+        berr = float(np.max(np.abs(bgrads[0][0, 0, rows].double().cpu().numpy() - bdq_rows)))
+        log(f"parity: prefill sampled max err {perr:.2e}, decode max err {derr:.2e}, grouped decode {gerr:.2e}, "
+            f"backward dq sampled {berr:.2e}")
+        parity = {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr,
+                  "backward_dq_sampled_max_err": berr}
 
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
@@ -437,8 +445,7 @@ def main():
         },
         "head_sizes": {"config": f"prefill B={P.B} H={P.H} N={P.N} bf16 non-causal", "by_d": head_sizes},
         "configs": configs,
-        "parity": {"prefill_sampled_max_err": perr, "decode_max_err": derr, "decode_gqa_max_err": gerr,
-                   "backward_dq_sampled_max_err": berr},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

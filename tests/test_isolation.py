@@ -63,3 +63,32 @@ def test_missing_library_fails_loudly(tmp_path):
     )
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert "raised" in out.stdout, out.stdout + out.stderr
+
+
+def test_bench_calls_the_oracle_only_in_its_host_leg():
+    """bench.py imports the oracle only inside cpu_baseline() or under the
+    `if not args.no_cpu_baseline` guard, so a run with --no-cpu-baseline (every
+    profiled run) never loads it."""
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    tree = ast.parse(src)
+    parents = {}
+    for node in ast.walk(tree):
+        for child in ast.iter_child_nodes(node):
+            parents[child] = node
+    found = 0
+    for node in ast.walk(tree):
+        names = []
+        if isinstance(node, ast.Import):
+            names = [a.name.split(".")[0] for a in node.names]
+        elif isinstance(node, ast.ImportFrom):
+            names = [(node.module or "").split(".")[0]]
+        if "oracle" not in names:
+            continue
+        found += 1
+        p, ok = parents.get(node), False
+        while p is not None and not ok:
+            ok = (isinstance(p, ast.FunctionDef) and p.name == "cpu_baseline") or (
+                isinstance(p, ast.If) and "no_cpu_baseline" in ast.get_source_segment(src, p.test))
+            p = parents.get(p)
+        assert ok, f"oracle imported outside the host leg at line {node.lineno}"
+    assert found >= 1
