@@ -1,0 +1,65 @@
+"""Prefill on seeded random shapes, drawn around the launcher's switch between workgroup
+forms: grids of B*H*ceil(N/256) blocks just below, at and above four per CU take the
+four-wave form, the eight-wave form, or (d = 64) two 32-row blocks per wave.
+
+Every case is checked on sampled rows against the fp64 oracle, and whole heads are
+compared bit for bit with one-head calls (a one-head grid always takes the four-wave,
+one-block form, and a row's arithmetic does not depend on the form).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_prefill_amd as ea
+import oracle
+import workloads as W
+from parity import check, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _cases(n=18, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 64, 96, 128]))
+        dtype = str(rng.choice(["f16", "bf16"]))
+        causal = bool(rng.integers(0, 2))
+        g = int(rng.choice([1, 1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([4, 8, 16]))
+        H = Hkv * g
+        # target blocks per CU of 256 rows: just below, at, or above the switch (4 per CU)
+        target = int(rng.choice([3.8 * 256, 4 * 256, 4.3 * 256]))
+        nb = max(1, round(target / (B * H)))
+        N = int(max(1, nb * 256 - int(rng.integers(0, 200))))  # ragged last block
+        scale = float(rng.choice([1 / np.sqrt(d), 0.125, -0.3]))
+        out.append((i, B, H, Hkv, N, d, dtype, causal, scale))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"c{c[0]}_B{c[1]}_H{c[2]}_Hkv{c[3]}_N{c[4]}_d{c[5]}_{c[6]}"
+                         + ("_causal" if c[7] else ""))
+def test_random_shape(case):
+    i, B, H, Hkv, N, d, dtype, causal, scale = case
+    q, k, v = W.prefill_inputs_gqa(B, H, Hkv, N, d, dtype, seed=100 + i)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = W.prefill_rows_sample(N, 24, seed=i)
+    g = H // Hkv
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 2)):
+        kvh = h // g
+        single = ea.prefill(qd[b:b + 1, h:h + 1].contiguous(), kd[b:b + 1, kvh:kvh + 1].contiguous(),
+                            vd[b:b + 1, kvh:kvh + 1].contiguous(), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out[b, h].view(torch.int16), single[0, 0].view(torch.int16)), (b, h)
+        ref = oracle.prefill_rows(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, kvh:kvh + 1]),
+                                  f64(v[b:b + 1, kvh:kvh + 1]), causal, scale, 0, 0, rows)
+        check(f64(out[b, h, rows]), ref, dtype, f"case {case} b={b} h={h}")
