@@ -284,7 +284,11 @@ def summarize(out: str):
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9 if dec_us and dec_bytes else None
     alg_pre_bytes = 4 * pre["B"] * pre["H"] * pre["N"] * pre["d"] * 2
     sha = source_hash(PREFILL_SOURCES)
+    # The same pass's bench line times the prefill with HIP events on its stream.
+    ev_ms = flop / (rec["roofline"]["achieved"] * 1e12) * 1e3 if rec and rec.get("roofline") else None
     derived = {
+        "prefill_events_ms": ev_ms,
+        "prefill_trace_vs_events": (p["avg_us"] / 1e3) / ev_ms if ev_ms and p.get("avg_us") else None,
         "prefill_tflops": pre_tf, "prefill_frac": pre_tf / PEAK_BF16_TFLOPS if pre_tf else None,
         "prefill_mfma_busy": p.get("mfma_busy"), "prefill_clock_ghz": p.get("clock_ghz"),
         "prefill_mfma_insts": p.get("mfma_insts"), "prefill_mfma_insts_algorithmic": flop / (32 * 32 * 16 * 2),
@@ -353,6 +357,9 @@ def render(out, rows, derived, agent, fc, wc, sha):
               f"{PEAK_BF16_TFLOPS:.0f} TFLOP/s (trace average); MFMA busy {_fmt(d['prefill_mfma_busy'], '.1%')} at "
               f"{_fmt(d['prefill_clock_ghz'], '.2f')} GHz; MFMA instructions {_fmt(d['prefill_mfma_insts'], '.4g')} vs "
               f"{d['prefill_mfma_insts_algorithmic']:.4g} for the algorithmic flop",
+              f"- prefill, the same pass's bench line (HIP events on the launch stream): "
+              f"{_fmt(d['prefill_events_ms'], '.4f')} ms per launch; trace average / events = "
+              f"{_fmt(d['prefill_trace_vs_events'], '.4f')}",
               f"- prefill HBM: {_fmt(hb / 1e6 if hb else None, '.1f')} MB per launch vs {ab / 1e6:.1f} MB algorithmic "
               f"(Q, K, V in, O out): {_fmt(hb / ab if hb else None, '.2f')}x",
               f"- decode: split + merge {_fmt(d['decode_us_split_plus_merge'], '.2f')} us (kernel time) = "

@@ -87,8 +87,9 @@ def run_dir(tmp_path):
     seq += [(SPLIT, 15_000), (MERGE, 5_000)] * ev.TRACE_DECODE_ITERS  # cold decode
     seq += [(PRE, 9_000_000)] * 3  # later launches with the lse output: not the step's
     _trace(os.path.join(out, "trace", "h", "run_kernel_trace.csv"), seq)
+    flop = 4.0 * 16 * 16384 * 16384 * 128
     rec = {"config": {"prefill": {"B": 1, "H": 16, "N": 16384, "d": 128, "causal": False}},
-           "decode": {"bytes": 64_000_000}}
+           "decode": {"bytes": 64_000_000}, "roofline": {"achieved": flop / 2.02e-3 / 1e12}}
     with open(os.path.join(out, "trace.log"), "w") as f:
         f.write("[bench] noise\n" + json.dumps(rec) + "\n")
     n_pmc = ev.PMC_WARMUP + ev.PMC_STEPS
@@ -119,6 +120,8 @@ def test_summary_derivations(run_dir):
     flop = 4.0 * 16 * 16384 * 16384 * 128
     assert d["prefill_tflops"] == pytest.approx(flop / 2e-3 / 1e12)  # the 2 ms step launches only
     assert d["prefill_frac"] == pytest.approx(d["prefill_tflops"] / 2500)
+    assert d["prefill_events_ms"] == pytest.approx(2.02)
+    assert d["prefill_trace_vs_events"] == pytest.approx(2.0 / 2.02)
     assert d["decode_us_split_plus_merge"] == pytest.approx(20.0)  # cold calls only
     assert d["decode_gbs"] == pytest.approx(64e6 / 20e-6 / 1e9)
     # FETCH factor 2 (copy read half), WRITE factor 1
