@@ -1,11 +1,12 @@
 """d = 64 prefill on large grids: two 32-row blocks per wave.
 
-Grids of at least four 256-row blocks per CU (256 CUs: B*H*ceil(N/256) >= 1024) run
-d = 64 with eight-wave, 512-row workgroups in which every wave owns two 32-row blocks
-and reads each K and V operand once for both.  The shapes below reach that form with
-ragged lengths; smaller grids (one head at a time) run one block per wave.  A row's
-arithmetic does not depend on the workgroup form, so every row of the large call must
-equal the one-head call bit for bit; sampled rows are also checked against the oracle.
+Grids of at least four 256-row blocks per CU (256 CUs: B*H*ceil(N/256) >= 1024) whose
+workgroups are not short (full: N > 2048, causal: N > 4096) run d = 64 with eight-wave,
+512-row workgroups in which every wave owns two 32-row blocks and reads each K and V
+operand once for both.  The shapes below reach that form with ragged lengths; smaller
+grids (one head at a time) run one block per wave.  A row's arithmetic does not depend
+on the workgroup form, so every row of the large call must equal the one-head call bit
+for bit; sampled rows are also checked against the oracle.
 """
 
 import numpy as np
@@ -21,16 +22,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 TWO_BLOCK = [
-    W.PrefillCase("prefill_b1_h64_n4001_d64_bf16_full", 1, 64, 4001, 64, "bf16", False, 0.125),
-    W.PrefillCase("prefill_b1_h64_n4001_d64_bf16_causal", 1, 64, 4001, 64, "bf16", True, 0.125),
-    W.PrefillCase("prefill_b4_h16_n3969_d64_f16_causal", 4, 16, 3969, 64, "f16", True, 0.125),
+    W.PrefillCase("prefill_b1_h32_n8001_d64_bf16_full", 1, 32, 8001, 64, "bf16", False, 0.125),
+    W.PrefillCase("prefill_b1_h32_n8001_d64_bf16_causal", 1, 32, 8001, 64, "bf16", True, 0.125),
+    W.PrefillCase("prefill_b2_h16_n7937_d64_f16_causal", 2, 16, 7937, 64, "f16", True, 0.125),
     W.PrefillCase("prefill_b4_h16_n3969_d64_f16_full", 4, 16, 3969, 64, "f16", False, -0.2),
 ]
 
 
 def reaches_two_block_form(case):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return case.B * case.H * -(-case.N // 256) >= 4 * cus
+    short = case.N <= (4096 if case.causal else 2048)
+    return case.d == 64 and case.B * case.H * -(-case.N // 256) >= 4 * cus and not short
 
 
 def one_head(q, k, v, b, h, causal, scale, lse=False):
@@ -66,6 +68,7 @@ def test_two_block_growing_scores(causal):
     """Keys growing along the sequence push the row maxima up past the optimistic
     margin again and again, so the redo path runs with both blocks of a wave live."""
     case = TWO_BLOCK[0]
+    assert reaches_two_block_form(W.PrefillCase("", case.B, case.H, case.N, case.d, case.dtype, causal, 0.0))
     q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=21)
     k = grow_keys(k, case.N)
     scale = 2.0 / np.sqrt(case.d)
@@ -73,7 +76,7 @@ def test_two_block_growing_scores(causal):
     out = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
     torch.cuda.synchronize()
     rows = W.prefill_rows_sample(case.N, 40, seed=21)
-    for h in (0, 33, 63):
+    for h in (0, 17, 31):
         single = one_head(qd, kd, vd, 0, h, causal, scale)
         torch.cuda.synchronize()
         assert torch.equal(out[0, h].view(torch.int16), single[0, 0].view(torch.int16)), h
@@ -84,9 +87,10 @@ def test_two_block_growing_scores(causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_two_block_grouped_heads(causal):
-    """64 query heads over 8 K/V heads at d = 64: each query head reads its group's
+    """32 query heads over 8 K/V heads at d = 64: each query head reads its group's
     K/V head; rows must equal the multi-head call on repeated K/V heads."""
-    B, Hq, Hkv, N, d = 1, 64, 8, 4000, 64
+    B, Hq, Hkv, N, d = 1, 32, 8, 8000, 64
+    assert reaches_two_block_form(W.PrefillCase("", B, Hq, N, d, "bf16", causal, 0.0))
     scale = 0.125
     q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=5)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
@@ -97,7 +101,7 @@ def test_two_block_grouped_heads(causal):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), rep.view(torch.int16))
     rows = W.prefill_rows_sample(N, 32, seed=5)
-    for h in (0, 7, 8, 63):
+    for h in (0, 3, 4, 31):
         ref = oracle.prefill_rows(f64(q), f64(k), f64(v), causal, scale, 0, h, rows)
         check(f64(out[0, h, rows]), ref, "bf16", f"two-block gqa h={h} causal={causal}")
 
@@ -107,6 +111,7 @@ def test_two_block_lse(causal):
     """The row log-sum-exp output of the two-block form: against the oracle on sampled
     rows, equal to the one-head call, and the output unchanged by asking for it."""
     case = TWO_BLOCK[0]
+    assert reaches_two_block_form(W.PrefillCase("", case.B, case.H, case.N, case.d, case.dtype, causal, 0.0))
     q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=9)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=case.scale, lse=True)
@@ -114,7 +119,7 @@ def test_two_block_lse(causal):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
     rows = W.prefill_rows_sample(case.N, 40, seed=9)
-    for h in (0, 63):
+    for h in (0, 31):
         _, single = one_head(qd, kd, vd, 0, h, causal, case.scale, lse=True)
         torch.cuda.synchronize()
         assert torch.equal(lse[0, h], single[0, 0]), h
