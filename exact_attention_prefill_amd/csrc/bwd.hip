@@ -582,9 +582,13 @@ static hipError_t launch_bwd_t(BwdParams p, int num_cus, hipStream_t s) {
   if (e != hipSuccess) return e;
   // Eight-wave dQ workgroups (256 rows, one per CU) stage each K/V tile for twice the
   // rows; as in the prefill they pay (about 2% at 16K tokens) once the grid gives every
-  // CU four of them, and smaller grids keep four waves.
+  // CU four of them, and smaller grids keep four waves.  So do short workgroups on any
+  // grid (full N <= 2048, causal N <= 4096), where two four-wave workgroups per CU
+  // overlap one's prologue and epilogue with the other's tiles: +2-5% for causal
+  // N = 2048..4096, +0.5-2.6% for full N = 1024..2048 (whole backward pass).
   const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-  e = blocks8 >= 4LL * num_cus ? launch_dq<DT, D, CAUSAL, 8>(p, s) : launch_dq<DT, D, CAUSAL, 4>(p, s);
+  const bool short_wgs = CAUSAL ? p.N <= 4096 : p.N <= 2048;
+  e = blocks8 >= 4LL * num_cus && !short_wgs ? launch_dq<DT, D, CAUSAL, 8>(p, s) : launch_dq<DT, D, CAUSAL, 4>(p, s);
   if (e != hipSuccess) return e;
   const int blk = 32 * bwd_cfg::NW;
   p.nblk = (p.N + blk - 1) / blk;

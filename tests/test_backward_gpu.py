@@ -119,14 +119,16 @@ def test_backward_headline_sampled(causal):
         assert torch.isfinite(t).all()
 
 
+@pytest.mark.parametrize("Hq,N", [(64, 4000), (32, 8000)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_eight_wave_dq_sampled(causal):
-    """64 query heads over 8 K/V heads at 4000 tokens: enough 256-row blocks for the
-    eight-wave dQ workgroups, with a ragged last block; sampled dq rows and dk/dv key
-    rows against the row-sampled oracle."""
+def test_backward_eight_wave_dq_sampled(causal, Hq, N):
+    """Query heads over 8 K/V heads with enough 256-row blocks for the eight-wave dQ
+    workgroups, and a ragged last block: at 4000 tokens the causal workgroups are short
+    and keep the four-wave form, at 8000 every case takes the eight-wave form; sampled
+    dq rows and dk/dv key rows against the row-sampled oracle."""
     from parity import backward_bounds_keys, backward_bounds_rows
 
-    B, Hq, Hkv, N, d = 1, 64, 8, 4000, 128
+    B, Hkv, d = 1, 8, 128
     scale = 1 / np.sqrt(d)
     q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=31)
     dout = W.prefill_inputs(B, Hq, N, d, "bf16", seed=32)[0]
@@ -136,7 +138,7 @@ def test_backward_eight_wave_dq_sampled(causal):
     torch.cuda.synchronize()
     qf, kf, vf, df = (f64(t) for t in (q, k, v, dout))
     rows = W.prefill_rows_sample(N, 10, seed=33)
-    for h in (0, 63):
+    for h in (0, Hq - 1):
         ref = oracle.backward_dq_rows(qf, kf, vf, df, causal, scale, 0, h, rows)
         bq = backward_bounds_rows(qf, kf, vf, df, causal, scale, 0, h, rows)
         check_grad(f64(dq[0, h, rows]), ref, bq, "bf16", f"dq h={h} causal={causal}")
