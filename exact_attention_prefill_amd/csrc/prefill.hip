@@ -500,12 +500,12 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   // it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
   // eight-wave grids, which then take 512-row workgroups.  d = 32 measured 5-6% slower
   // with it and keeps one block per wave.
-  // Short workgroups stay on the four-wave form whatever the grid: when a workgroup
-  // averages 32 tiles or fewer (full: N <= 2048; causal: N <= 4096), the two
-  // workgroups a CU holds overlap one's prologue and epilogue with the other's tiles,
-  // and the causal diagonal's spread between waves is halved.  Measured: causal
-  // N = 1024..4096 +4-21% at d = 128 (+36-40% at d = 64 against two blocks per wave),
-  // full N = 512..2048 +1-11%; longer sequences lose 1-2% on it.
+  // Short workgroups stay on the four-wave form whatever the grid (full: N <= 2048;
+  // causal: N <= 8192, d = 96 N <= 6144): the two workgroups a CU holds overlap one's
+  // prologue and epilogue with the other's tiles, and the causal diagonal's spread
+  // between waves is halved.  Measured: causal N = 1024..8192 +1-21% at d = 128,
+  // +5-11% at d = 32, +33-41% at d = 64 against two blocks per wave; full N = 512..2048
+  // +1-11%.  Longer sequences lose 1-2% on it (d = 96: 2.6% at causal N = 8192).
   // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
   // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
   // workgroup per CU.
@@ -513,7 +513,7 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
     const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-    const bool short_wgs = CAUSAL ? p.N <= 4096 : p.N <= 2048;
+    const bool short_wgs = CAUSAL ? p.N <= (D == 96 ? 6144 : 8192) : p.N <= 2048;
     if (blocks8 >= 4LL * num_cus && !short_wgs) {
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);

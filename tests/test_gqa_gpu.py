@@ -51,9 +51,9 @@ def test_prefill_gqa_equals_repeated_heads(d):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_gqa_eight_wave_form_sampled(causal):
-    """32 query heads over 8 K/V heads at 8000 tokens: enough 256-row blocks, and long
+    """32 query heads over 8 K/V heads at 8300 tokens: enough 256-row blocks, and long
     enough workgroups (causal too), for the eight-wave form, with a ragged last block."""
-    B, Hq, Hkv, N, d = 1, 32, 8, 8000, 128
+    B, Hq, Hkv, N, d = 1, 32, 8, 8300, 128
     scale = 1 / np.sqrt(d)
     q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=5)
     out = ea.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)

@@ -1,7 +1,7 @@
 """d = 64 prefill on large grids: two 32-row blocks per wave.
 
 Grids of at least four 256-row blocks per CU (256 CUs: B*H*ceil(N/256) >= 1024) whose
-workgroups are not short (full: N > 2048, causal: N > 4096) run d = 64 with eight-wave,
+workgroups are not short (full: N > 2048, causal: N > 8192) run d = 64 with eight-wave,
 512-row workgroups in which every wave owns two 32-row blocks and reads each K and V
 operand once for both.  The shapes below reach that form with ragged lengths; smaller
 grids (one head at a time) run one block per wave.  A row's arithmetic does not depend
@@ -22,16 +22,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 TWO_BLOCK = [
-    W.PrefillCase("prefill_b1_h32_n8001_d64_bf16_full", 1, 32, 8001, 64, "bf16", False, 0.125),
-    W.PrefillCase("prefill_b1_h32_n8001_d64_bf16_causal", 1, 32, 8001, 64, "bf16", True, 0.125),
-    W.PrefillCase("prefill_b2_h16_n7937_d64_f16_causal", 2, 16, 7937, 64, "f16", True, 0.125),
+    W.PrefillCase("prefill_b1_h32_n8300_d64_bf16_full", 1, 32, 8300, 64, "bf16", False, 0.125),
+    W.PrefillCase("prefill_b1_h32_n8300_d64_bf16_causal", 1, 32, 8300, 64, "bf16", True, 0.125),
+    W.PrefillCase("prefill_b2_h16_n8300_d64_f16_causal", 2, 16, 8300, 64, "f16", True, 0.125),
     W.PrefillCase("prefill_b4_h16_n3969_d64_f16_full", 4, 16, 3969, 64, "f16", False, -0.2),
 ]
 
 
 def reaches_two_block_form(case):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    short = case.N <= (4096 if case.causal else 2048)
+    short = case.N <= (8192 if case.causal else 2048)
     return case.d == 64 and case.B * case.H * -(-case.N // 256) >= 4 * cus and not short
 
 
@@ -89,7 +89,7 @@ def test_two_block_growing_scores(causal):
 def test_two_block_grouped_heads(causal):
     """32 query heads over 8 K/V heads at d = 64: each query head reads its group's
     K/V head; rows must equal the multi-head call on repeated K/V heads."""
-    B, Hq, Hkv, N, d = 1, 32, 8, 8000, 64
+    B, Hq, Hkv, N, d = 1, 32, 8, 8300, 64
     assert reaches_two_block_form(W.PrefillCase("", B, Hq, N, d, "bf16", causal, 0.0))
     scale = 0.125
     q, k, v = W.prefill_inputs_gqa(B, Hq, Hkv, N, d, "bf16", seed=5)
