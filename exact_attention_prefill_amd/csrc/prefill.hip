@@ -488,6 +488,14 @@ static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Longest sequence whose workgroups count as short: these keep the four-wave form on
+// any grid.  Measured per head size (see launch_prefill_w).
+template <int D, bool CAUSAL>
+constexpr int short_workgroup_limit() {
+  if constexpr (CAUSAL) return D == 64 ? 12288 : (D == 96 ? 6144 : 8192);
+  else return D == 64 ? 4096 : 2048;
+}
+
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStream_t s) {
   // Waves of 32 query rows, two per SIMD.  Eight waves per workgroup (256 query rows,
@@ -500,12 +508,14 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   // it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
   // eight-wave grids, which then take 512-row workgroups.  d = 32 measured 5-6% slower
   // with it and keeps one block per wave.
-  // Short workgroups stay on the four-wave form whatever the grid (full: N <= 2048;
-  // causal: N <= 8192, d = 96 N <= 6144): the two workgroups a CU holds overlap one's
-  // prologue and epilogue with the other's tiles, and the causal diagonal's spread
-  // between waves is halved.  Measured: causal N = 1024..8192 +1-21% at d = 128,
-  // +5-11% at d = 32, +33-41% at d = 64 against two blocks per wave; full N = 512..2048
-  // +1-11%.  Longer sequences lose 1-2% on it (d = 96: 2.6% at causal N = 8192).
+  // Short workgroups stay on the four-wave form whatever the grid (full: N <= 2048,
+  // d = 64 N <= 4096; causal: N <= 8192, d = 96 N <= 6144, d = 64 N <= 12288): the
+  // two workgroups a CU holds overlap one's prologue and epilogue with the other's
+  // tiles, and the causal diagonal's spread between waves is halved.  Measured: causal
+  // N = 1024..8192 +1-21% at d = 128, +5-11% at d = 32, +13-41% at d = 64 (N up to
+  // 12288) against two blocks per wave; full N = 512..2048 +1-11%, d = 64 at 4096 +2%.
+  // Longer sequences lose on it: 1-2% at d = 128, d = 96 2.6% at causal N = 8192, d = 64
+  // 5-6.5% at full N >= 8192 and 6% at causal N = 16384.
   // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
   // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
   // workgroup per CU.
@@ -513,7 +523,7 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
     const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-    const bool short_wgs = CAUSAL ? p.N <= (D == 96 ? 6144 : 8192) : p.N <= 2048;
+    const bool short_wgs = p.N <= short_workgroup_limit<D, CAUSAL>();
     if (blocks8 >= 4LL * num_cus && !short_wgs) {
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);

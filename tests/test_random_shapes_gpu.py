@@ -1,8 +1,8 @@
 """Prefill on seeded random shapes, drawn around the launcher's switch between workgroup
 forms: grids of B*H*ceil(N/256) blocks just below, at and above four per CU take the
 four-wave form, the eight-wave form, or (d = 64) two 32-row blocks per wave; short
-workgroups (full N <= 2048, causal N <= 8192, d = 96 causal N <= 6144) keep the
-four-wave form on any grid.
+workgroups (full N <= 2048, d = 64 N <= 4096; causal N <= 8192, d = 96 N <= 6144,
+d = 64 N <= 12288) keep the four-wave form on any grid.
 
 Every case is checked on sampled rows against the fp64 oracle, and whole heads are
 compared bit for bit with one-head calls (a one-head grid always takes the four-wave,
