@@ -502,7 +502,8 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   // one workgroup per CU) stage each K/V tile once for twice the rows of the
   // four-wave form (128 rows, two workgroups per CU), halving L2-to-LDS traffic per
   // MFMA; it pays (+2-3% at d = 128, 16K tokens) when the grid still gives every CU
-  // at least four such workgroups, and small grids keep the finer four-wave blocks.
+  // at least two (full) or four (causal) such workgroups, and small grids keep the
+  // finer four-wave blocks.
   // The 64-row form (QB = 2) halves LDS operand reads per MFMA.  At d = 128 it runs
   // one wave per SIMD and measured 5-8% slower, so it is not selected there; at d = 64
   // it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
@@ -522,9 +523,12 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   if constexpr (D > 128) {
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
+    // Full grids take the eight-wave forms from two 256-row blocks per CU (+3-5% at
+    // two to three per CU, d = 64 +13%); causal grids, whose workgroups vary in length,
+    // from four (at three per CU they measured 3% slower on it).
     const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
     const bool short_wgs = p.N <= short_workgroup_limit<D, CAUSAL>();
-    if (blocks8 >= 4LL * num_cus && !short_wgs) {
+    if (blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs) {
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
     }

@@ -86,13 +86,15 @@ def test_gpt2_sweep_4096_sampled(case):
     sampled_parity(case, 2, heads, nrows=64)
 
 
-# Grids of at least four 256-row blocks per CU take the eight-wave workgroups unless
+# Grids of at least four 256-row blocks per CU (full: two) take the eight-wave workgroups unless
 # the workgroups are short (full: N <= 2048, d = 64: 4096; causal: N <= 8192, d = 96:
 # 6144, d = 64: 12288), which keep the four-wave form; these shapes reach both with a
 # ragged last block (N not a multiple of 256): the d = 128 causal N = 8300 and
-# d = 96 causal N = 7937 cases and the d = 128 full ones the eight-wave form, the
-# others the four-wave form on a large grid.
+# d = 96 causal N = 7937 cases and the d = 128 full ones (H = 9 at N = 16001: two to
+# four blocks per CU) the eight-wave form, the others the four-wave form on a large
+# grid.
 LARGE_RAGGED = [
+    W.PrefillCase("prefill_b1_h9_n16001_d128_bf16_full", 1, 9, 16001, 128, "bf16", False, 1 / np.sqrt(128)),
     W.PrefillCase("prefill_b1_h32_n8300_d128_bf16_causal", 1, 32, 8300, 128, "bf16", True, 1 / np.sqrt(128)),
     W.PrefillCase("prefill_b1_h32_n8000_d128_bf16_causal", 1, 32, 8000, 128, "bf16", True, 1 / np.sqrt(128)),
     W.PrefillCase("prefill_b2_h16_n7937_d96_f16_causal", 2, 16, 7937, 96, "f16", True, 1 / np.sqrt(96)),

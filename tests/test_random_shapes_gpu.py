@@ -1,6 +1,7 @@
 """Prefill on seeded random shapes, drawn around the launcher's switch between workgroup
-forms: grids of B*H*ceil(N/256) blocks just below, at and above four per CU take the
-four-wave form, the eight-wave form, or (d = 64) two 32-row blocks per wave; short
+forms: grids of B*H*ceil(N/256) blocks just below, at and above four per CU (causal;
+full grids switch at two per CU) take the four-wave form, the eight-wave form, or
+(d = 64) two 32-row blocks per wave; short
 workgroups (full N <= 2048, d = 64 N <= 4096; causal N <= 8192, d = 96 N <= 6144,
 d = 64 N <= 12288) keep the four-wave form on any grid.
 

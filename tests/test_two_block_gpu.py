@@ -1,9 +1,9 @@
 """d = 64 prefill on large grids: two 32-row blocks per wave.
 
-Grids of at least four 256-row blocks per CU (256 CUs: B*H*ceil(N/256) >= 1024) whose
-workgroups are not short (full: N > 4096, causal: N > 12288) run d = 64 with eight-wave,
-512-row workgroups in which every wave owns two 32-row blocks and reads each K and V
-operand once for both.  The shapes below reach that form with ragged lengths; smaller
+Grids of at least two (full) or four (causal) 256-row blocks per CU (256 CUs:
+B*H*ceil(N/256) >= 512 or 1024) whose workgroups are not short (full: N > 4096,
+causal: N > 12288) run d = 64 with eight-wave, 512-row workgroups in which every wave
+owns two 32-row blocks and reads each K and V operand once for both.  The shapes below reach that form with ragged lengths; smaller
 grids (one head at a time) run one block per wave.  A row's arithmetic does not depend
 on the workgroup form, so every row of the large call must equal the one-head call bit
 for bit; sampled rows are also checked against the oracle.
@@ -32,7 +32,8 @@ TWO_BLOCK = [
 def reaches_two_block_form(case):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     short = case.N <= (12288 if case.causal else 4096)
-    return case.d == 64 and case.B * case.H * -(-case.N // 256) >= 4 * cus and not short
+    need = 4 if case.causal else 2  # 256-row blocks per CU
+    return case.d == 64 and case.B * case.H * -(-case.N // 256) >= need * cus and not short
 
 
 def one_head(q, k, v, b, h, causal, scale, lse=False):
