@@ -585,10 +585,13 @@ static hipError_t launch_bwd_t(BwdParams p, int num_cus, hipStream_t s) {
   // CU four of them, and smaller grids keep four waves.  So do short workgroups on any
   // grid (full N <= 2048, causal N <= 4096), where two four-wave workgroups per CU
   // overlap one's prologue and epilogue with the other's tiles: +2-5% for causal
-  // N = 2048..4096, +0.5-2.6% for full N = 1024..2048 (whole backward pass).
+  // N = 2048..4096, +0.5-2.6% for full N = 1024..2048 (whole backward pass).  As in the
+  // prefill, full grids take eight waves from two blocks per CU (+0.4-2.1% at two to
+  // three per CU), causal grids from four.
   const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
   const bool short_wgs = CAUSAL ? p.N <= 4096 : p.N <= 2048;
-  e = blocks8 >= 4LL * num_cus && !short_wgs ? launch_dq<DT, D, CAUSAL, 8>(p, s) : launch_dq<DT, D, CAUSAL, 4>(p, s);
+  e = blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs ? launch_dq<DT, D, CAUSAL, 8>(p, s)
+                                                                : launch_dq<DT, D, CAUSAL, 4>(p, s);
   if (e != hipSuccess) return e;
   const int blk = 32 * bwd_cfg::NW;
   p.nblk = (p.N + blk - 1) / blk;

@@ -119,13 +119,14 @@ def test_backward_headline_sampled(causal):
         assert torch.isfinite(t).all()
 
 
-@pytest.mark.parametrize("Hq,N", [(64, 4000), (32, 8000)])
+@pytest.mark.parametrize("Hq,N", [(64, 4000), (32, 8000), (16, 8001)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_eight_wave_dq_sampled(causal, Hq, N):
     """Query heads over 8 K/V heads with enough 256-row blocks for the eight-wave dQ
     workgroups, and a ragged last block: at 4000 tokens the causal workgroups are short
-    and keep the four-wave form, at 8000 every case takes the eight-wave form; sampled
-    dq rows and dk/dv key rows against the row-sampled oracle."""
+    and keep the four-wave form, at 8000 every case takes the eight-wave form, and at
+    16 heads of 8001 (two blocks per CU) the full case takes it and the causal one does
+    not; sampled dq rows and dk/dv key rows against the row-sampled oracle."""
     from parity import backward_bounds_keys, backward_bounds_rows
 
     B, Hkv, d = 1, 8, 128
