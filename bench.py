@@ -286,6 +286,22 @@ def main():
     bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
     log(f"backward {bwd_ms:.3f} ms = {bwd_tflops:.1f} TFLOP/s")
 
+    def settled_ms(call, n=10, warm_ms=80.0):
+        """Median event time of n calls, after calling for warm_ms of wall time first:
+        making each shape's inputs on the host leaves the GPU idle long enough for its
+        clock to drop, and a couple of warm-up calls do not bring it back."""
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            call()
+            torch.cuda.synchronize()
+        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs_:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs_]))
+
     # Prefill at every head size the library builds, at the headline's B, H and N
     # (bf16, non-causal; flop 4*B*H*N*N*d), timed with events outside the step.
     head_sizes = {}
@@ -293,15 +309,7 @@ def main():
         for hd in (32, 64, 96, 128, 256):
             hq, hk, hv = (t.to(dev) for t in W.prefill_inputs(P.B, P.H, P.N, hd, "bf16", seed=0))
             hout = torch.empty_like(hq)
-            for _ in range(2):
-                ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
-            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-            for a, b in hev:
-                a.record()
-                ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout)
-                b.record()
-            torch.cuda.synchronize()
-            hms = float(np.median([a.elapsed_time(b) for a, b in hev]))
+            hms = settled_ms(lambda: ea.prefill(hq, hk, hv, scale=1 / math.sqrt(hd), out=hout))
             htf = 4.0 * P.B * P.H * P.N * P.N * hd / (hms * 1e-3) / 1e12
             head_sizes[str(hd)] = {"ms": round(hms, 4), "tflops": round(htf, 1), "frac": round(htf / PEAK_BF16_TFLOPS, 4)}
             del hq, hk, hv, hout
@@ -309,21 +317,13 @@ def main():
 
     # Every prefill workload shape (small, GPT-2-like at 2048 tokens, the dense d=128
     # token splits, the long sequences) and the batch-1 decode, each timed alone with
-    # events: median of 5 launches after 2 warm-ups; decode cold as above.
+    # events: median of 10 launches after the clock has settled; decode cold as above.
     configs = {}
     if not args.no_configs:
         for case in W.SMALL_F16 + W.GPT2_F16 + W.DENSE_D128 + W.LONG:
             cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=0))
             cout = torch.empty_like(cq)
-            for _ in range(2):
-                ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)
-            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-            for a, b in cev:
-                a.record()
-                ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)
-                b.record()
-            torch.cuda.synchronize()
-            cms = float(np.median([a.elapsed_time(b) for a, b in cev]))
+            cms = settled_ms(lambda: ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout))
             ctf = case.flop / (cms * 1e-3) / 1e12
             configs[case.name] = {"ms": round(cms, 4), "tflops": round(ctf, 1), "frac": round(ctf / PEAK_BF16_TFLOPS, 4)}
             del cq, ck, cv, cout
