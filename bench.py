@@ -9,7 +9,8 @@ One step is one pass of the whole hot path over one batch of synthetic input:
     uniform in [1, 4096] from seed 0 (page 3, "What can it do": a different current
     length per sequence), split-K with the automatic chunk, then the merge.
 Inputs are made once from seed 0 and are resident in HBM before timing starts.
-W untimed steps, then K timed steps between two device synchronisations.
+100 ms of untimed steps settle the clock (input generation leaves the GPU idle), then W
+untimed steps, then K timed steps between two device synchronisations.
 
 Prints ONE JSON line.  `value` is prefill TFLOP/s over the whole timed region
 (algorithmic flop 4*B*H*N*N*d per step / wall time per step, decode included in the
@@ -186,6 +187,13 @@ def main():
         if ev:
             ev[2].record()
 
+    # Making the inputs on the host leaves the GPU idle for seconds, and its clock drops;
+    # 100 ms of untimed steps bring it back to the steady state before the W warm-up
+    # steps and the K timed ones.
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) < 0.1:
+        step()
+        torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
