@@ -25,7 +25,9 @@ the prefill's shape, also outside the steps; its flop count is 2.5 times the
 forward's (the five products of the chain rule, each of the forward's size).
 `head_sizes` times the prefill at d = 32, 64, 96, 128 and 256 with the headline's
 B, H and N (bf16, non-causal), outside the steps.
-`configs` times every other workload shape alone, outside the steps: the small
+`configs` times every other workload shape alone, outside the steps (events around
+each call; the calls small enough to be launch-bound also as one HIP graph of 20
+calls replayed, `graph_ms`, which leaves the host's launch overhead out): the small
 prefill (B=1, H=1, N=128, d=64, fp16), the GPT-2-like prompt (B=1, H=12, N=2048, d=64,
 fp16, full and causal), the dense d=128 token splits (B*N = 16384 at H=16), the long
 sequences (B=1, H=24, d=128, bf16: N=32768 full, N=16384 causal) and the batch-1
@@ -310,6 +312,36 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in evs_]))
 
+    def graph_ms(call, reps=20, n=5, warm_ms=80.0):
+        """Per-call GPU time of `reps` calls captured in one HIP graph, median of n
+        replays after the clock settles: the host's launch overhead is left out, as a
+        serving loop replaying a captured graph sees it.  The calls capture kernel
+        launches only (no allocation, no memset)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # capture wants the calls warmed up off the default stream
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            g.replay()
+            torch.cuda.synchronize()
+        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs_:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs_])) / reps
+        del g
+        return ms
+
     # Prefill at every head size the library builds, at the headline's B, H and N
     # (bf16, non-causal; flop 4*B*H*N*N*d), timed with events outside the step.
     head_sizes = {}
@@ -331,9 +363,14 @@ def main():
         for case in W.SMALL_F16 + W.GPT2_F16 + W.DENSE_D128 + W.LONG:
             cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=0))
             cout = torch.empty_like(cq)
-            cms = settled_ms(lambda: ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout))
+            ccall = lambda: ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)  # noqa: E731
+            cms = settled_ms(ccall)
             ctf = case.flop / (cms * 1e-3) / 1e12
             configs[case.name] = {"ms": round(cms, 4), "tflops": round(ctf, 1), "frac": round(ctf / PEAK_BF16_TFLOPS, 4)}
+            if case.flop < 1e11:  # launch-latency-sized calls: also their GPU time alone
+                gms = graph_ms(ccall)
+                gtf = case.flop / (gms * 1e-3) / 1e12
+                configs[case.name].update({"graph_ms": round(gms, 4), "graph_tflops": round(gtf, 1)})
             del cq, ck, cv, cout
         D1 = W.DECODE[0]
         eq, ek, ev_, el = (t.to(dev) for t in W.decode_inputs(D1.B, D1.H, D1.max_len, D1.d, D1.dtype, seed=0))
