@@ -27,7 +27,7 @@ namespace attn {
 
 namespace decode_cfg {
 constexpr int kUnroll = 4;          // row loads of K (and of V) per lane per buffer (two buffers)
-constexpr int kMergeThreads = 256;  // merge workgroup: 4 split groups x 64
+constexpr int kMergeBatch = 8;      // splits per merge group per round of loads
 constexpr int kMfmaMinGroup = 3;    // smallest group of query heads decoded on the matrix cores
 }  // namespace decode_cfg
 
@@ -420,16 +420,16 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeParams p) {
 }
 
 // Exact merge: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the non-empty
-// splits (empty ones carry m = -inf); a length of 0 writes zeros.  Four groups of 64
-// threads take every fourth split, eight splits per round, each round's loads issued
-// together (one memory latency per round rather than per split).  The groups' sums
-// meet in LDS in a fixed order, so the result is deterministic.
-template <int DT, int D>
-__global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+// splits (empty ones carry m = -inf); a length of 0 writes zeros.  NG groups of 64
+// threads take every NG-th split, eight splits per round, each round's loads issued
+// together (one memory latency per round rather than per split): four groups cover up
+// to 32 splits in one round, eight groups up to 64.  The groups' sums meet in LDS in a
+// fixed order, so the result is deterministic.
+template <int DT, int D, int NG>
+__global__ __launch_bounds__(64 * NG) void decode_merge_kernel(DecodeParams p) {
   using namespace decode_cfg;
-  constexpr int NG = kMergeThreads / 64;
   constexpr int DPT = (D + 63) / 64;  // d elements per thread (the last pass may be partial)
-  constexpr int NBAT = 8;      // splits per group per round
+  constexpr int NBAT = kMergeBatch;   // splits per group per round
   __shared__ float sm_M[NG];
   __shared__ float sm_den[NG];
   __shared__ float sm_num[NG][D];
@@ -507,13 +507,24 @@ __global__ __launch_bounds__(decode_cfg::kMergeThreads) void decode_merge_kernel
   }
 }
 
+// The merge: eight groups of 64 threads when the splits exceed what four groups load in
+// one round (32), four otherwise.  Measured at B = 1 (64 splits): 12.4 -> 12.0 us for
+// the call; at 22 splits four groups and eight measure the same.
+template <int DT, int D>
+static hipError_t launch_merge(const DecodeParams& p, hipStream_t st) {
+  if (p.n_split > 4 * decode_cfg::kMergeBatch)
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D, 8>), dim3(p.H, p.B), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D, 4>), dim3(p.H, p.B), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int G>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(p.n_split, p.H / G, p.B), dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(decode_cfg::kMergeThreads), 0, st, p);
-  return hipGetLastError();
+  return launch_merge<DT, D>(p, st);
 }
 
 bool decode_uses_mfma(int H, int Hkv);
@@ -523,8 +534,7 @@ static hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_mfma_kernel<DT, D>), dim3(p.n_split, p.Hkv, p.B), dim3(64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(p.H, p.B), dim3(decode_cfg::kMergeThreads), 0, st, p);
-  return hipGetLastError();
+  return launch_merge<DT, D>(p, st);
 }
 
 template <int DT, int D>
