@@ -74,9 +74,9 @@ DERIVED_SLOTS = {"FETCH_SIZE": {"TCC": 3}, "WRITE_SIZE": {"TCC": 2}}
 KERNELS = {
     "prefill": "attn::prefill_kernel<1, 128, false, 8, 1>",
     "decode_split": "attn::decode_split_kernel<0, 64, 1>",
-    "decode_merge": "attn::decode_merge_kernel<0, 64>",
+    "decode_merge": "attn::decode_merge_kernel<0, 64, 4>",
     "gqa_split": "attn::decode_split_mfma_kernel<1, 128>",
-    "gqa_merge": "attn::decode_merge_kernel<1, 128>",
+    "gqa_merge": "attn::decode_merge_kernel<1, 128, 4>",
     "bwd_delta": "attn::bwd_delta_kernel<1, 128>",
     "bwd_dq": "attn::bwd_dq_kernel<1, 128, false, 8>",
     "bwd_dkdv": "attn::bwd_dkdv_kernel<1, 128, false>",
@@ -231,30 +231,40 @@ def summarize(out: str):
         if p:
             pmc[name] = read_counters(p)
 
-    n_pre_trace = TRACE_WARMUP + TRACE_STEPS
-    n_pre_pmc = PMC_WARMUP + PMC_STEPS
+    run_shape = {"trace": (TRACE_WARMUP, TRACE_STEPS, TRACE_DECODE_ITERS),
+                 "pmc": (PMC_WARMUP, PMC_STEPS, PMC_DECODE_ITERS)}
 
-    def kernel_slices(key, dispatches, n_plain):
+    def kernel_slices(key, dispatches, kind):
+        """The dispatches of one kernel that the figures describe.  The bench runs, in
+        order: untimed clock-settling steps (as many as fit in its settle time), W
+        warm-up steps and K timed steps (a prefill and a decode each), then the cold
+        decode calls, then the prefill launches that also write the log-sum-exp.  The
+        settling steps are counted from the decode's dispatches; the prefill figures
+        take the K timed launches and the decode figures the cold calls."""
         sig = KERNELS[key]
-        if key == "prefill":  # the step's launches come first; later ones carry the lse output
-            return select(dispatches, sig, 0, n_plain)
-        if key in ("decode_split", "decode_merge"):  # cold calls follow the step's
-            return select(dispatches, sig, n_plain)
+        W_, K_, I_ = run_shape[kind]
+        settle = len(select(dispatches, KERNELS["decode_split"])) - (W_ + K_) - I_
+        if settle < 0:
+            settle = 0
+        if key == "prefill":
+            return select(dispatches, sig, settle + W_, K_)
+        if key in ("decode_split", "decode_merge"):
+            return select(dispatches, sig, settle + W_ + K_)
         return select(dispatches, sig)
 
     fc = calibration(pmc.get("fetch", []), "FETCH_SIZE", CALIBRATE_MIB * 1024)
     wc = calibration(pmc.get("write", []), "WRITE_SIZE", CALIBRATE_MIB * 1024)
     rows = {}
     for key in KERNELS:
-        t = kernel_slices(key, trace, n_pre_trace)
+        t = kernel_slices(key, trace, "trace")
         r = {"dispatches": len(t), "avg_us": statistics.mean(d[1] for d in t) / 1e3 if t else None,
              "min_us": min(d[1] for d in t) / 1e3 if t else None}
-        f = median_counter(kernel_slices(key, pmc.get("fetch", []), n_pre_pmc), "FETCH_SIZE")
-        w = median_counter(kernel_slices(key, pmc.get("write", []), n_pre_pmc), "WRITE_SIZE")
+        f = median_counter(kernel_slices(key, pmc.get("fetch", []), "pmc"), "FETCH_SIZE")
+        w = median_counter(kernel_slices(key, pmc.get("write", []), "pmc"), "WRITE_SIZE")
         if f is not None and w is not None and fc and wc:
             r["fetch_kib_raw"], r["write_kib_raw"] = f, w
             r["hbm_bytes"] = f * fc * 1024 + w * wc * 1024
-        m = kernel_slices(key, pmc.get("mfma", []), n_pre_pmc)
+        m = kernel_slices(key, pmc.get("mfma", []), "pmc")
         busy = median_counter(m, "SQ_VALU_MFMA_BUSY_CYCLES")
         grbm = median_counter(m, "GRBM_GUI_ACTIVE")
         insts = median_counter(m, "SQ_INSTS_MFMA")
@@ -268,7 +278,7 @@ def summarize(out: str):
             r["clock_ghz"] = (grbm / n_xcd) / dur if dur >= MIN_CLOCK_NS else None
             co = median_counter(m, "SQ_VALU_MFMA_COEXEC_CYCLES")
             r["coexec"] = co / (n_simd * grbm / n_xcd) if co is not None else None
-        lds = kernel_slices(key, pmc.get("lds", []), n_pre_pmc)
+        lds = kernel_slices(key, pmc.get("lds", []), "pmc")
         bank, active = median_counter(lds, "SQ_LDS_BANK_CONFLICT"), median_counter(lds, "SQ_LDS_IDX_ACTIVE")
         if bank is not None and active:
             r["lds_conflict_frac"] = bank / active
@@ -350,8 +360,8 @@ def render(out, rows, derived, agent, fc, wc, sha):
     d = derived
     hb, ab = d["prefill_hbm_bytes"], d["prefill_algorithmic_bytes"]
     lines += ["",
-              "Prefill rows are the step's launches (warm-ups and timed steps), before the launches that also",
-              "write the log-sum-exp; decode rows are the cold calls (a 512 MiB read before each).", "",
+              "Prefill rows are the step's timed launches (after the clock-settling and warm-up steps, before the",
+              "launches that also write the log-sum-exp); decode rows are the cold calls (a 512 MiB read before each).", "",
               "## Derived", "",
               f"- prefill: {_fmt(d['prefill_tflops'], '.1f')} TFLOP/s = {_fmt(d['prefill_frac'], '.1%')} of "
               f"{PEAK_BF16_TFLOPS:.0f} TFLOP/s (trace average); MFMA busy {_fmt(d['prefill_mfma_busy'], '.1%')} at "

@@ -80,9 +80,12 @@ def _pmc(path, seq):
 def run_dir(tmp_path):
     out = str(tmp_path)
     _agent(os.path.join(out, "trace", "h", "run_agent_info.csv"))
-    n_pre = ev.TRACE_WARMUP + ev.TRACE_STEPS
     seq = []
-    for _ in range(n_pre):  # the step: prefill then decode (warm)
+    for _ in range(7):  # clock-settling steps: neither figure may include them
+        seq += [(PRE, 5_000_000), (SPLIT, 777_777), (MERGE, 777_777)]
+    for _ in range(ev.TRACE_WARMUP):  # warm-up steps: slower than the timed ones
+        seq += [(PRE, 3_000_000), (SPLIT, 999_999), (MERGE, 999_999)]
+    for _ in range(ev.TRACE_STEPS):  # the timed steps: prefill then decode (warm)
         seq += [(PRE, 2_000_000), (SPLIT, 999_999), (MERGE, 999_999)]
     seq += [(SPLIT, 15_000), (MERGE, 5_000)] * ev.TRACE_DECODE_ITERS  # cold decode
     seq += [(PRE, 9_000_000)] * 3  # later launches with the lse output: not the step's
@@ -97,6 +100,8 @@ def run_dir(tmp_path):
 
     def pmc_seq(counter, pre_val, split_val, copy_val):
         s = [("__amd_rocclr_copyBuffer", 100, {counter: 3.0})]
+        for _ in range(5):  # clock-settling steps
+            s += [(PRE, 1_000_000, {counter: 7e11}), (SPLIT, 1, {counter: 7e9}), (MERGE, 1, {counter: 7e9})]
         for _ in range(n_pmc):
             s += [(PRE, 1_000_000, {counter: pre_val}), (SPLIT, 1, {counter: 1e9}), (MERGE, 1, {counter: 1e9})]
         s += [(SPLIT, 1, {counter: split_val}), (MERGE, 1, {counter: 0.0})] * ev.PMC_DECODE_ITERS
@@ -110,7 +115,9 @@ def run_dir(tmp_path):
     # (1.5 GHz); 8 SIMDs busy 6e6 cycles in all = 50%; 1.875e5 MFMAs x 32 cycles / (8 x 1.5e6) = 50%;
     # both units busy 1.2e6 cycles = 10%.
     mf = [(PRE, 1_000_000, {"GRBM_GUI_ACTIVE": 3.0e6, "SQ_VALU_MFMA_BUSY_CYCLES": 6.0e6, "SQ_INSTS_MFMA": 1.875e5,
-                            "SQ_VALU_MFMA_COEXEC_CYCLES": 1.2e6})] * n_pmc
+                            "SQ_VALU_MFMA_COEXEC_CYCLES": 1.2e6}),
+          (SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * n_pmc
+    mf += [(SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * ev.PMC_DECODE_ITERS
     _pmc(os.path.join(out, "mfma", "h", "run_counter_collection.csv"), mf)
     return out
 
