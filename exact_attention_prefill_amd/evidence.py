@@ -72,7 +72,7 @@ DERIVED_SLOTS = {"FETCH_SIZE": {"TCC": 3}, "WRITE_SIZE": {"TCC": 2}}
 
 # Kernels of the headline workloads, by template signature.
 KERNELS = {
-    "prefill": "attn::prefill_kernel<1, 128, false, 8, 1>",
+    "prefill": "attn::prefill_kernel<1, 128, false, 8, 1, false>",
     "decode_split": "attn::decode_split_kernel<0, 64, 1>",
     "decode_merge": "attn::decode_merge_kernel<0, 64, 4>",
     "gqa_split": "attn::decode_split_mfma_kernel<1, 128>",
