@@ -590,14 +590,16 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
     }
-    // d = 64 on the four-wave form (64 KiB of LDS for four stages, so two workgroups
-    // still share a CU): four stages for causal grids and for grids of at most two
-    // 128-row blocks per CU, where the loads issued two tiles ahead pay; full grids
-    // of more blocks keep two stages.  Measured: causal +1-7%, the GPT-2-like prompts
-    // (B = 1, H = 12, N = 1024..4096) +2.5-7%; full B = 4, N = 4096 -1.6 to -2.8%.
-    if constexpr (D == 64) {
+    // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two
+    // workgroups still share a CU): four stages for grids of at most two 128-row blocks
+    // per CU, and at d = 64 for causal grids, where the loads issued two tiles ahead
+    // pay; other grids keep two stages.  Measured: the GPT-2-like prompts (B = 1,
+    // H = 12, N = 1024..4096) +2.5-7% at d = 64 and +5-7% at d = 32; causal d = 64
+    // +1-7%; full B = 4, N = 4096 d = 64 -1.6 to -2.8%; causal d = 32 on large grids
+    // -6 to -8%.
+    if constexpr (D <= 64) {
       const long long blocks4 = (long long)p.B * p.H * ((p.N + 127) / 128);
-      if (CAUSAL || blocks4 <= 2LL * num_cus) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
+      if (blocks4 <= 2LL * num_cus || (D == 64 && CAUSAL)) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
     }
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }
