@@ -597,9 +597,14 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     // H = 12, N = 1024..4096) +2.5-7% at d = 64 and +5-7% at d = 32; causal d = 64
     // +1-7%; full B = 4, N = 4096 d = 64 -1.6 to -2.8%; causal d = 32 on large grids
     // -6 to -8%.
+    // d = 96 and 128 need 96 and 128 KiB for four stages, one workgroup per CU: they
+    // take them on grids of at most one 128-row block per CU, which run one workgroup
+    // per CU anyway (+2-8% at B = 1, H = 4..16, N = 2048..8192, full and causal).
+    const long long blocks4 = (long long)p.B * p.H * ((p.N + 127) / 128);
     if constexpr (D <= 64) {
-      const long long blocks4 = (long long)p.B * p.H * ((p.N + 127) / 128);
       if (blocks4 <= 2LL * num_cus || (D == 64 && CAUSAL)) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
+    } else {
+      if (blocks4 <= (long long)num_cus) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
     }
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }

@@ -34,7 +34,7 @@ def test_small_config(case, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 17, 63, 64, 65, 127, 128, 129, 200, 333])
 def test_ragged_lengths(N, causal, d, dtype):
@@ -119,7 +119,7 @@ def test_scale_values(scale, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_growing_scores_raise_the_running_max(causal, d, dtype):
     """Key magnitudes that grow along the sequence push each row's maximum up again
@@ -133,6 +133,29 @@ def test_growing_scores_raise_the_running_max(causal, d, dtype):
     out = run(q, k, v, causal, scale)
     ref = oracle.prefill(f64(q), f64(k), f64(v), causal, scale)
     check(f64(out), ref, dtype, f"growing scores d{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(128, "bf16", False), (128, "f16", True), (96, "bf16", True)])
+def test_four_stage_form_matches_two_stage(d, dtype, causal):
+    """d = 96 and 128 grids of at most one 128-row block per CU keep four K/V tiles in
+    LDS (loads two tiles ahead); larger grids keep two.  A row's arithmetic is the same
+    in both, so the heads of a 4-head call equal the same heads inside a 16-head call bit
+    for bit; sampled rows are checked against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 8001
+    assert 4 * -(-N // 128) <= cus < 16 * -(-N // 128)  # 4 heads: four stages; 16 heads: two
+    q, k, v = W.prefill_inputs(1, 16, N, d, dtype, 31)
+    scale = 1.0 / np.sqrt(d)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    big = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
+    small = ea.prefill(qd[:, 4:8].contiguous(), kd[:, 4:8].contiguous(), vd[:, 4:8].contiguous(), causal=causal,
+                       scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, 4:8].view(torch.int16), small.view(torch.int16))
+    rows = W.prefill_rows_sample(N, 24, seed=31)
+    for h in (4, 7):
+        ref = oracle.prefill_rows(f64(q), f64(k), f64(v), causal, scale, 0, h, rows)
+        check(f64(big[0, h, rows]), ref, dtype, f"four/two stages d{d} h={h} causal={causal}")
 
 
 def test_zero_query_gives_mean():
