@@ -21,7 +21,8 @@ runs on.  `decode` reports the decode path's HBM rate, timed with events after a
 heads of 128, bf16, cache 4096 rows), whose bytes count the cache once per K/V head;
 it runs after the timed steps and is not part of them.
 `backward` times the backward pass (dq, dk, dv from out, lse and a seeded dout) at
-the prefill's shape, also outside the steps; its flop count is 2.5 times the
+the prefill's shape, also outside the steps and once the clock settles (as the
+prefill with the log-sum-exp output, `prefill_lse`); its flop count is 2.5 times the
 forward's (the five products of the chain rule, each of the forward's size).
 `head_sizes` times the prefill at d = 32, 64, 96, 128 and 256 with the headline's
 B, H and N (bf16, non-causal), outside the steps.
@@ -258,44 +259,6 @@ def main():
     gqa_gbs = gqa_bytes / (gqa_us * 1e-6) / 1e9
     log(f"decode (grouped heads {GQ.H}/{gkv}) cold {gqa_us:.2f} us = {gqa_gbs:.0f} GB/s")
 
-    # The prefill with its row log-sum-exp output (the forward the backward pass needs),
-    # timed like the step's prefill.
-    lse_buf = torch.empty(P.B, P.H, P.N, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out, lse=lse_buf)
-    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    for a, b in lev:
-        a.record()
-        ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out, lse=lse_buf)
-        b.record()
-    torch.cuda.synchronize()
-    lse_ms = float(np.median([a.elapsed_time(b) for a, b in lev]))
-    log(f"prefill with lse {lse_ms:.3f} ms = {P.flop / (lse_ms * 1e-3) / 1e12:.1f} TFLOP/s")
-
-    # Backward pass at the prefill's shape (out and lse from the forward with the
-    # log-sum-exp output, a seeded dout), timed with events outside the step.
-    bdo = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=1)[0].to(dev)
-    bout, blse = ea.prefill(q, k, v, causal=P.causal, scale=P.scale, lse=True)
-    bws = torch.empty(ea.backward_workspace_bytes(P.B, P.H, P.N) // 4, dtype=torch.float32, device=dev)
-    bgrads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
-
-    def bcall():
-        ea.backward(q, k, v, bout, bdo, blse, causal=P.causal, scale=P.scale, dq=bgrads[0], dk=bgrads[1],
-                    dv=bgrads[2], workspace=bws)
-
-    for _ in range(2):
-        bcall()
-    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.bwd_iters)]
-    for a, b in bev:
-        a.record()
-        bcall()
-        b.record()
-    torch.cuda.synchronize()
-    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bev]))
-    bwd_flop = 2.5 * P.flop  # five products of the forward's size (QK^T, dO V^T, dV, dQ, dK)
-    bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
-    log(f"backward {bwd_ms:.3f} ms = {bwd_tflops:.1f} TFLOP/s")
-
     def settled_ms(call, n=10, warm_ms=80.0):
         """Median event time of n calls, after calling for warm_ms of wall time first:
         making each shape's inputs on the host leaves the GPU idle long enough for its
@@ -311,6 +274,29 @@ def main():
             b.record()
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in evs_]))
+
+    # The prefill with its row log-sum-exp output (the forward the backward pass needs),
+    # after its clock settles: the cold decode calls before it leave the GPU mostly idle.
+    lse_buf = torch.empty(P.B, P.H, P.N, dtype=torch.float32, device=dev)
+    lse_ms = settled_ms(lambda: ea.prefill(q, k, v, causal=P.causal, scale=P.scale, out=out, lse=lse_buf))
+    log(f"prefill with lse {lse_ms:.3f} ms = {P.flop / (lse_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+
+    # Backward pass at the prefill's shape (out and lse from the forward with the
+    # log-sum-exp output, a seeded dout), timed with events outside the step once its
+    # clock settles (median of the calls).
+    bdo = W.prefill_inputs(P.B, P.H, P.N, P.d, P.dtype, seed=1)[0].to(dev)
+    bout, blse = ea.prefill(q, k, v, causal=P.causal, scale=P.scale, lse=True)
+    bws = torch.empty(ea.backward_workspace_bytes(P.B, P.H, P.N) // 4, dtype=torch.float32, device=dev)
+    bgrads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+
+    def bcall():
+        ea.backward(q, k, v, bout, bdo, blse, causal=P.causal, scale=P.scale, dq=bgrads[0], dk=bgrads[1],
+                    dv=bgrads[2], workspace=bws)
+
+    bwd_ms = settled_ms(bcall, n=args.bwd_iters)
+    bwd_flop = 2.5 * P.flop  # five products of the forward's size (QK^T, dO V^T, dV, dQ, dK)
+    bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    log(f"backward {bwd_ms:.3f} ms = {bwd_tflops:.1f} TFLOP/s")
 
     def graph_ms(call, reps=20, n=5, warm_ms=80.0):
         """Per-call GPU time of `reps` calls captured in one HIP graph, median of n
