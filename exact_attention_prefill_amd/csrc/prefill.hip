@@ -586,8 +586,11 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     // from four (at three per CU they measured 3% slower on it).
     const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
     const bool short_wgs = p.N <= short_workgroup_limit<D, CAUSAL>();
+    // Four LDS stages there cost no occupancy (one eight-wave workgroup per CU either
+    // way) but pay only on the full d = 64 grids: +1.4-1.9% at B*H*N = 0.26M..0.79M
+    // rows; d = 128 lost 3%, causal d = 64 4%, d = 96 up to 1%, d = 32 measured flat.
     if (blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs) {
-      if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2>(p, s);
+      if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2, !CAUSAL>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
     }
     // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two

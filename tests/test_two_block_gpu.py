@@ -3,7 +3,8 @@
 Grids of at least two (full) or four (causal) 256-row blocks per CU (256 CUs:
 B*H*ceil(N/256) >= 512 or 1024) whose workgroups are not short (full: N > 4096,
 causal: N > 12288) run d = 64 with eight-wave, 512-row workgroups in which every wave
-owns two 32-row blocks and reads each K and V operand once for both.  The shapes below reach that form with ragged lengths; smaller
+owns two 32-row blocks and reads each K and V operand once for both (full grids keep
+four K/V tiles in LDS, causal ones two).  The shapes below reach that form with ragged lengths; smaller
 grids (one head at a time) run one block per wave.  A row's arithmetic does not depend
 on the workgroup form, so every row of the large call must equal the one-head call bit
 for bit; sampled rows are also checked against the oracle.
