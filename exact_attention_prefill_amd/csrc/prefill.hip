@@ -602,12 +602,15 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     // -6 to -8%.
     // d = 96 and 128 need 96 and 128 KiB for four stages, one workgroup per CU: they
     // take them on grids of at most one 128-row block per CU, which run one workgroup
-    // per CU anyway (+2-8% at B = 1, H = 4..16, N = 2048..8192, full and causal).
+    // per CU anyway (+2-8% at B = 1, H = 4..16, N = 2048..8192, full and causal), and
+    // causal grids of at most two (+8-13% at B = 1, H = 12..16, N = 4096).  Full grids
+    // of two blocks per CU lost 23-36% on it (two rounds of workgroups), causal grids
+    // of three to eight 14-40%.
     const long long blocks4 = (long long)p.B * p.H * ((p.N + 127) / 128);
     if constexpr (D <= 64) {
       if (blocks4 <= 2LL * num_cus || (D == 64 && CAUSAL)) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
     } else {
-      if (blocks4 <= (long long)num_cus) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
+      if (blocks4 <= (CAUSAL ? 2LL : 1LL) * num_cus) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
     }
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }

@@ -135,28 +135,31 @@ def test_growing_scores_raise_the_running_max(causal, d, dtype):
     check(f64(out), ref, dtype, f"growing scores d{d} {dtype} causal={causal}")
 
 
-@pytest.mark.parametrize("d,dtype,causal", [(128, "bf16", False), (128, "f16", True), (96, "bf16", True),
-                                             (64, "bf16", False), (32, "f16", False), (32, "bf16", True)])
-def test_four_stage_form_matches_two_stage(d, dtype, causal):
-    """Small grids keep four K/V tiles in LDS (loads two tiles ahead): at most one
-    128-row block per CU at d = 96 and 128, two at d = 32 and 64.  The 16-head grids
-    below take another form (two stages, or eight waves).  A row's arithmetic is the
-    same in every form, so the heads of a 4-head call equal the same heads inside a
-    16-head call bit for bit; sampled rows are checked against the oracle."""
+@pytest.mark.parametrize("d,dtype,causal,nh", [(128, "bf16", False, 4), (128, "f16", True, 4), (96, "bf16", True, 4),
+                                                (128, "bf16", True, 8), (96, "f16", True, 8), (64, "bf16", False, 4),
+                                                (32, "f16", False, 4), (32, "bf16", True, 8)])
+def test_four_stage_form_matches_two_stage(d, dtype, causal, nh):
+    """Small grids keep four K/V tiles in LDS (loads two tiles ahead): at d = 96 and
+    128 grids of at most one 128-row block per CU (causal: two), at d = 32 and 64 of at
+    most two.  The 16-head grids below take another form (two stages, or eight waves).
+    A row's arithmetic is the same in every form, so the heads of an nh-head call
+    equal the same heads inside a 16-head call bit for bit; sampled rows are checked
+    against the oracle."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     N = 8001
-    limit = cus if d > 64 else 2 * cus
-    assert 4 * -(-N // 128) <= limit < 16 * -(-N // 128)  # 4 heads: four stages; 16 heads: not
+    limit = (2 if causal else 1) * cus if d > 64 else 2 * cus
+    assert nh * -(-N // 128) <= limit < 16 * -(-N // 128)  # nh heads: four stages; 16 heads: not
     q, k, v = W.prefill_inputs(1, 16, N, d, dtype, 31)
     scale = 1.0 / np.sqrt(d)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     big = ea.prefill(qd, kd, vd, causal=causal, scale=scale)
-    small = ea.prefill(qd[:, 4:8].contiguous(), kd[:, 4:8].contiguous(), vd[:, 4:8].contiguous(), causal=causal,
+    sl = slice(4, 4 + nh)
+    small = ea.prefill(qd[:, sl].contiguous(), kd[:, sl].contiguous(), vd[:, sl].contiguous(), causal=causal,
                        scale=scale)
     torch.cuda.synchronize()
-    assert torch.equal(big[:, 4:8].view(torch.int16), small.view(torch.int16))
+    assert torch.equal(big[:, sl].view(torch.int16), small.view(torch.int16))
     rows = W.prefill_rows_sample(N, 24, seed=31)
-    for h in (4, 7):
+    for h in (4, 3 + nh):
         ref = oracle.prefill_rows(f64(q), f64(k), f64(v), causal, scale, 0, h, rows)
         check(f64(big[0, h, rows]), ref, dtype, f"four/two stages d{d} h={h} causal={causal}")
 
