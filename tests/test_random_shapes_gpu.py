@@ -5,6 +5,9 @@ full grids switch at two per CU) take the four-wave form, the eight-wave form, o
 workgroups (full N <= 2048, d = 64 N <= 4096; causal N <= 8192, d = 96 N <= 6144,
 d = 64 N <= 12288) keep the four-wave form on any grid.
 
+A second set draws small grids, of B*H*ceil(N/128) blocks around one and two per CU,
+where the number of LDS stages changes (four on small grids, by head size and mask).
+
 Every case is checked on sampled rows against the fp64 oracle, and whole heads are
 compared bit for bit with one-head calls (a one-head grid always takes the four-wave,
 one-block form, and a row's arithmetic does not depend on the form).
@@ -46,7 +49,31 @@ def _cases(n=18, seed=20261203):
 CASES = _cases()
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"c{c[0]}_B{c[1]}_H{c[2]}_Hkv{c[3]}_N{c[4]}_d{c[5]}_{c[6]}"
+def _small_cases(n=14, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 96, 128]))
+        dtype = str(rng.choice(["f16", "bf16"]))
+        causal = bool(rng.integers(0, 2))
+        g = int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([2, 4, 8]))
+        H = Hkv * g
+        # target 128-row blocks per CU: around the one- and two-per-CU switches
+        target = float(rng.choice([0.9, 1.0, 1.1, 1.9, 2.0, 2.1]))
+        nb = max(1, round(target * 256 / (B * H)))
+        N = int(max(1, nb * 128 - int(rng.integers(0, 100))))  # ragged last block
+        scale = float(rng.choice([1 / np.sqrt(d), 0.125, -0.3]))
+        out.append((100 + i, B, H, Hkv, N, d, dtype, causal, scale))
+    return out
+
+
+SMALL_CASES = _small_cases()
+
+
+@pytest.mark.parametrize("case", CASES + SMALL_CASES,
+                         ids=lambda c: f"c{c[0]}_B{c[1]}_H{c[2]}_Hkv{c[3]}_N{c[4]}_d{c[5]}_{c[6]}"
                          + ("_causal" if c[7] else ""))
 def test_random_shape(case):
     i, B, H, Hkv, N, d, dtype, causal, scale = case
