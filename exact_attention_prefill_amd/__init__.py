@@ -42,6 +42,8 @@ EXPORTS = (
     "attn_prefill_ex",
     "attn_backward",
     "attn_backward_workspace_bytes",
+    "attn_prefill_plan",
+    "attn_build_id",
 )
 
 _lib = None
@@ -94,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_gqa.restype = i
         L.attn_decode_gqa_choose_split.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.attn_decode_gqa_choose_split.restype = i
+        L.attn_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
+        L.attn_prefill_plan.restype = i
+        L.attn_build_id.argtypes = []
+        L.attn_build_id.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -260,8 +266,23 @@ def decode_gqa_choose_split(B: int, Hq: int, Hkv: int, max_len: int, d: int, num
     return c.value, n.value
 
 
+def prefill_plan(B: int, H: int, N: int, d: int, causal: bool, num_cus: int) -> dict:
+    """The workgroup form attn_prefill takes for this shape on a device with num_cus CUs:
+    {"waves": waves per workgroup, "rows_per_wave": query rows per wave, "stages": K/V
+    LDS stages}.  Host only."""
+    w, r, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().attn_prefill_plan(B, H, N, d, int(bool(causal)), num_cus, ctypes.byref(w), ctypes.byref(r),
+                                   ctypes.byref(s)))
+    return {"waves": w.value, "rows_per_wave": r.value, "stages": s.value}
+
+
 def decode_workspace_bytes(B: int, H: int, n_split: int, d: int) -> int:
     return int(lib().attn_decode_workspace_bytes(B, H, n_split, d))
+
+
+def build_id() -> str:
+    """The source identifier compiled into the loaded libattn.so (see build.source_hash)."""
+    return lib().attn_build_id().decode()
 
 
 def status_string(status: int) -> str:

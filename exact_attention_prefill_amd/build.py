@@ -20,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "bwd.hip"]
+HEADERS = [os.path.join(CSRC, "attn_device.h"), os.path.join(CSRC, "attn_launch.h"), os.path.join(ROOT, "include", "attn.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -41,16 +42,48 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) over every source and header the library is built
+    from; the build embeds it, and attn_build_id() returns it from the loaded library."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in [os.path.join(CSRC, s) for s in SOURCES] + HEADERS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object in parallel (one hipcc per file), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"] + [f'-DATTN_SOURCE_HASH="{source_hash()}"']
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *compile_flags, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, r
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for obj, r in results:
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed compiling {obj}")
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libattn.so")
+        raise RuntimeError("hipcc failed linking libattn.so")
     os.replace(tmp, out)
     return out
 

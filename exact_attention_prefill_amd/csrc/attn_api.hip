@@ -11,19 +11,7 @@
 
 #include "attn.h"
 
-namespace attn {
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
-                          int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
-hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
-                         int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
-                         hipStream_t st);
-int decode_heads_per_wave(int H, int Hkv);
-bool decode_uses_mfma(int H, int Hkv);
-int decode_mfma_waves_per_cu(int d);
-hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, float* ws, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
-                           int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
-}  // namespace attn
+#include "attn_launch.h"
 
 namespace {
 
@@ -107,6 +95,11 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_err; }
 
+#ifndef ATTN_SOURCE_HASH
+#define ATTN_SOURCE_HASH "unknown"
+#endif
+const char* attn_build_id(void) { return ATTN_SOURCE_HASH; }
+
 static int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
                         int N, int d, int dtype, int causal, float scale, void* stream) {
   int st;
@@ -142,6 +135,21 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* out, int
 int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int N,
                     int d, int dtype, int causal, float scale, void* stream) {
   return prefill_impl(q, k, v, out, lse, B, Hq, Hkv, N, d, dtype, causal, scale, stream);
+}
+
+int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* waves_per_workgroup,
+                      int* rows_per_wave, int* lds_stages) {
+  if (B < 1 || H < 1 || N < 1 || num_cus < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H, N and num_cus must be >= 1");
+  if (!head_dim_ok(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
+  if (!waves_per_workgroup || !rows_per_wave || !lds_stages)
+    return fail(ATTN_ERR_INVALID_ARG, "the plan outputs must be non-NULL host pointers");
+  const attn::PrefillForm f = attn::prefill_form(B, H, N, d, causal, num_cus);
+  *waves_per_workgroup = f.nw;
+  *rows_per_wave = 32 * f.qb;
+  *lds_stages = f.s4 ? 4 : 2;
+  return ok();
 }
 
 // The split for `pairs` wave columns (one wave per column and split) aiming at

@@ -1,0 +1,34 @@
+// Host-side launchers of the attention kernels and the prefill launch rule, shared by
+// the C interface (attn_api.hip) and the kernel files.  Internal: not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// The workgroup form a prefill launch takes: waves per workgroup, 32-row query blocks
+// per wave, and whether K/V are staged in four LDS stages (one barrier per two tiles)
+// rather than two.
+struct PrefillForm {
+  int nw;
+  int qb;
+  int s4;
+};
+
+// The rule launch_prefill applies (host only; no HIP call).
+PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus);
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                          int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
+                         int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
+                         hipStream_t st);
+int decode_heads_per_wave(int H, int Hkv);
+bool decode_uses_mfma(int H, int Hkv);
+int decode_mfma_waves_per_cu(int d);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, float* ws, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                           int d, int dt, int causal, float scale, int num_cus, hipStream_t s);
+
+}  // namespace attn

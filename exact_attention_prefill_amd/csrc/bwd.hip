@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "attn_device.h"
+#include "attn_launch.h"
 
 namespace attn {
 

@@ -22,6 +22,7 @@
 // the sequence's length writes only (m, l) = (-inf, 0); its acc is never read.
 #include "attn.h"
 #include "attn_device.h"
+#include "attn_launch.h"
 
 namespace attn {
 

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "attn_device.h"
+#include "attn_launch.h"
 
 namespace attn {
 
@@ -569,71 +570,82 @@ static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
 }
 
 // Longest sequence whose workgroups count as short: these keep the four-wave form on
-// any grid.  Measured per head size (see launch_prefill_w).
-template <int D, bool CAUSAL>
-constexpr int short_workgroup_limit() {
-  if constexpr (CAUSAL) return D == 64 ? 12288 : (D == 96 ? 6144 : 8192);
-  else return D == 64 ? 4096 : 2048;
+// any grid.  Measured per head size (see prefill_form).
+static int short_workgroup_limit(int d, bool causal) {
+  if (causal) return d == 64 ? 12288 : (d == 96 ? 6144 : 8192);
+  return d == 64 ? 4096 : 2048;
+}
+
+// The workgroup form a launch takes, from the grid alone (host-side rule).
+// Waves of 32 query rows, two per SIMD.  Eight waves per workgroup (256 query rows,
+// one workgroup per CU) stage each K/V tile once for twice the rows of the
+// four-wave form (128 rows, two workgroups per CU), halving L2-to-LDS traffic per
+// MFMA; it pays (+2-3% at d = 128, 16K tokens) when the grid still gives every CU
+// at least two (full) or four (causal) such workgroups, and small grids keep the
+// finer four-wave blocks.
+// The 64-row form (QB = 2) halves LDS operand reads per MFMA.  At d = 128 it runs
+// one wave per SIMD and measured 5-8% slower, so it is not selected there; at d = 64
+// it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
+// eight-wave grids, which then take 512-row workgroups.  d = 32 measured 5-6% slower
+// with it and keeps one block per wave.
+// Short workgroups stay on the four-wave form whatever the grid (full: N <= 2048,
+// d = 64 N <= 4096; causal: N <= 8192, d = 96 N <= 6144, d = 64 N <= 12288): the
+// two workgroups a CU holds overlap one's prologue and epilogue with the other's
+// tiles, and the causal diagonal's spread between waves is halved.  Measured: causal
+// N = 1024..8192 +1-21% at d = 128, +5-11% at d = 32, +13-41% at d = 64 (N up to
+// 12288) against two blocks per wave; full N = 512..2048 +1-11%, d = 64 at 4096 +2%.
+// Longer sequences lose on it: 1-2% at d = 128, d = 96 2.6% at causal N = 8192, d = 64
+// 5-6.5% at full N >= 8192 and 6% at causal N = 16384.
+// d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
+// 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
+// workgroup per CU.
+PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
+  if (d > 128) return {4, 1, 0};
+  // Full grids take the eight-wave forms from two 256-row blocks per CU (+3-5% at
+  // two to three per CU, d = 64 +13%); causal grids, whose workgroups vary in length,
+  // from four (at three per CU they measured 3% slower on it).
+  const long long blocks8 = (long long)B * H * ((N + 255) / 256);
+  const bool short_wgs = N <= short_workgroup_limit(d, causal != 0);
+  // Four LDS stages there cost no occupancy (one eight-wave workgroup per CU either
+  // way) but pay only on the full d = 64 grids: +1.4-1.9% at B*H*N = 0.26M..0.79M
+  // rows; d = 128 lost 3%, causal d = 64 4%, d = 96 up to 1%, d = 32 measured flat.
+  if (blocks8 >= (causal ? 4LL : 2LL) * num_cus && !short_wgs) {
+    if (d == 64) return {8, 2, causal ? 0 : 1};
+    return {8, 1, 0};
+  }
+  // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two
+  // workgroups still share a CU): four stages for grids of at most two 128-row blocks
+  // per CU, and at d = 64 for causal grids, where the loads issued two tiles ahead
+  // pay; other grids keep two stages.  Measured: the GPT-2-like prompts (B = 1,
+  // H = 12, N = 1024..4096) +2.5-7% at d = 64 and +5-7% at d = 32; causal d = 64
+  // +1-7%; full B = 4, N = 4096 d = 64 -1.6 to -2.8%; causal d = 32 on large grids
+  // -6 to -8%.
+  // d = 96 and 128 need 96 and 128 KiB for four stages, one workgroup per CU: they
+  // take them on grids of at most one 128-row block per CU, which run one workgroup
+  // per CU anyway (+2-8% at B = 1, H = 4..16, N = 2048..8192, full and causal), and
+  // causal grids of at most two (+8-13% at B = 1, H = 12..16, N = 4096).  Full grids
+  // of two blocks per CU lost 23-36% on it (two rounds of workgroups), causal grids
+  // of three to eight 14-40%.
+  const long long blocks4 = (long long)B * H * ((N + 127) / 128);
+  if (d <= 64) {
+    if (blocks4 <= 2LL * num_cus || (d == 64 && causal)) return {4, 1, 1};
+  } else {
+    if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) return {4, 1, 1};
+  }
+  return {4, 1, 0};
 }
 
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStream_t s) {
-  // Waves of 32 query rows, two per SIMD.  Eight waves per workgroup (256 query rows,
-  // one workgroup per CU) stage each K/V tile once for twice the rows of the
-  // four-wave form (128 rows, two workgroups per CU), halving L2-to-LDS traffic per
-  // MFMA; it pays (+2-3% at d = 128, 16K tokens) when the grid still gives every CU
-  // at least two (full) or four (causal) such workgroups, and small grids keep the
-  // finer four-wave blocks.
-  // The 64-row form (QB = 2) halves LDS operand reads per MFMA.  At d = 128 it runs
-  // one wave per SIMD and measured 5-8% slower, so it is not selected there; at d = 64
-  // it keeps two waves per SIMD and measured 9-10% faster (3-4% causal) on the
-  // eight-wave grids, which then take 512-row workgroups.  d = 32 measured 5-6% slower
-  // with it and keeps one block per wave.
-  // Short workgroups stay on the four-wave form whatever the grid (full: N <= 2048,
-  // d = 64 N <= 4096; causal: N <= 8192, d = 96 N <= 6144, d = 64 N <= 12288): the
-  // two workgroups a CU holds overlap one's prologue and epilogue with the other's
-  // tiles, and the causal diagonal's spread between waves is halved.  Measured: causal
-  // N = 1024..8192 +1-21% at d = 128, +5-11% at d = 32, +13-41% at d = 64 (N up to
-  // 12288) against two blocks per wave; full N = 512..2048 +1-11%, d = 64 at 4096 +2%.
-  // Longer sequences lose on it: 1-2% at d = 128, d = 96 2.6% at causal N = 8192, d = 64
-  // 5-6.5% at full N >= 8192 and 6% at causal N = 16384.
-  // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
-  // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
-  // workgroup per CU.
+  const PrefillForm f = prefill_form(p.B, p.H, p.N, D, CAUSAL, num_cus);
   if constexpr (D > 128) {
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
-    // Full grids take the eight-wave forms from two 256-row blocks per CU (+3-5% at
-    // two to three per CU, d = 64 +13%); causal grids, whose workgroups vary in length,
-    // from four (at three per CU they measured 3% slower on it).
-    const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
-    const bool short_wgs = p.N <= short_workgroup_limit<D, CAUSAL>();
-    // Four LDS stages there cost no occupancy (one eight-wave workgroup per CU either
-    // way) but pay only on the full d = 64 grids: +1.4-1.9% at B*H*N = 0.26M..0.79M
-    // rows; d = 128 lost 3%, causal d = 64 4%, d = 96 up to 1%, d = 32 measured flat.
-    if (blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs) {
+    if (f.nw == 8) {
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2, !CAUSAL>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
     }
-    // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two
-    // workgroups still share a CU): four stages for grids of at most two 128-row blocks
-    // per CU, and at d = 64 for causal grids, where the loads issued two tiles ahead
-    // pay; other grids keep two stages.  Measured: the GPT-2-like prompts (B = 1,
-    // H = 12, N = 1024..4096) +2.5-7% at d = 64 and +5-7% at d = 32; causal d = 64
-    // +1-7%; full B = 4, N = 4096 d = 64 -1.6 to -2.8%; causal d = 32 on large grids
-    // -6 to -8%.
-    // d = 96 and 128 need 96 and 128 KiB for four stages, one workgroup per CU: they
-    // take them on grids of at most one 128-row block per CU, which run one workgroup
-    // per CU anyway (+2-8% at B = 1, H = 4..16, N = 2048..8192, full and causal), and
-    // causal grids of at most two (+8-13% at B = 1, H = 12..16, N = 4096).  Full grids
-    // of two blocks per CU lost 23-36% on it (two rounds of workgroups), causal grids
-    // of three to eight 14-40%.
-    const long long blocks4 = (long long)p.B * p.H * ((p.N + 127) / 128);
-    if constexpr (D <= 64) {
-      if (blocks4 <= 2LL * num_cus || (D == 64 && CAUSAL)) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
-    } else {
-      if (blocks4 <= (CAUSAL ? 2LL : 1LL) * num_cus) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
-    }
+    if (f.s4) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }
 }

@@ -63,6 +63,19 @@ typedef enum {
 int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                  int dtype, int causal, float scale, void* stream);
 
+/* Host-only: the workgroup form attn_prefill / attn_prefill_gqa / attn_prefill_ex take
+ * for this shape on a device with num_cus compute units (page 3, "Kernel design": the
+ * work is cut into independent (query block, head, batch) pieces; the block height
+ * follows the grid so that the device stays full).  Writes to HOST pointers:
+ *   waves_per_workgroup : 4 or 8 waves of 64 lanes;
+ *   rows_per_wave       : query rows each wave owns (32 or 64), so one workgroup
+ *                         covers waves_per_workgroup * rows_per_wave query rows;
+ *   lds_stages          : K/V tiles held in on-chip memory per operand (2 or 4).
+ * Every form computes each row with the same arithmetic.  Validation as for
+ * attn_prefill (Hkv does not affect the form).  No HIP call. */
+int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* waves_per_workgroup,
+                      int* rows_per_wave, int* lds_stages);
+
 /* Decode (page 3, "What can it do": generation phase; "Installation": decode(q,
  * k_cache, v_cache, seq_lens, scale)).
  *   q        : [B][H][1][d] one query row per sequence and head;
@@ -191,6 +204,12 @@ const char* attn_status_string(int status);
 
 /* Host-only: thread-local detail for the last non-OK return on this thread ("" if none). */
 const char* attn_last_error(void);
+
+/* Host-only: identifier of the sources this library was built from (the first 16 hex
+ * digits of a sha256 over its kernel, interface and header files, fixed at compile
+ * time; "unknown" for a build that did not set it).  Lets a caller check that the
+ * library it loaded matches the sources it expects. */
+const char* attn_build_id(void);
 
 #ifdef __cplusplus
 }

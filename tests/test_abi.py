@@ -256,3 +256,10 @@ def test_backward_validation(kw, status):
 def test_backward_workspace_bytes():
     assert ea.backward_workspace_bytes(2, 8, 100) == 2 * (2 * 8 * 100 * 4)
     assert ea.backward_workspace_bytes(0, 8, 100) == 0
+
+
+def test_library_was_built_from_these_sources():
+    from exact_attention_prefill_amd import build
+
+    assert ea.build_id() == build.source_hash()
+

@@ -34,8 +34,9 @@ def test_prefill_parity(d, N, causal, dtype):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", NEW_D)
 def test_prefill_many_tiles_sampled(d, causal):
-    """Enough 256-row blocks for the eight-wave workgroups at d = 32 and 96 (d = 256
-    always runs four waves), with a ragged last tile."""
+    """A mid-sized grid (16 heads of 3000 rows: 192 256-row blocks, fewer than the
+    eight-wave forms need, so four-wave workgroups of two stages at d = 32 and 96; d = 256
+    always runs four waves) with a ragged last tile."""
     B, H, N = 1, 16, 3000
     scale = 1 / np.sqrt(d)
     q, k, v = W.prefill_inputs(B, H, N, d, "bf16", seed=d)
@@ -164,17 +165,22 @@ def test_prefill_causality_and_canaries(d):
     assert torch.equal(a[:, :, : i + 1].view(torch.int16), b[:, :, : i + 1].view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", NEW_D)
-def test_prefill_sixteen_k_sampled(d):
-    """16384 tokens, as the benchmark's head-size sweep runs them: sampled rows of the
-    first and last heads against the row-sampled oracle."""
-    B, H, N = 1, 4, 16384
+def test_prefill_sixteen_k_sampled(d, dtype):
+    """B=1, H=16, N=16384, non-causal: the shape and launch form of the benchmark's
+    head-size sweep (eight-wave workgroups at d = 32 and 96, four waves at d = 256, as
+    the launch plan asserts), sampled rows of three heads against the row-sampled
+    oracle."""
+    B, H, N = 1, 16, 16384
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ea.prefill_plan(B, H, N, d, False, cus)["waves"] == (4 if d == 256 else 8)
     scale = 1 / np.sqrt(d)
-    q, k, v = W.prefill_inputs(B, H, N, d, "bf16", seed=d + 3)
+    q, k, v = W.prefill_inputs(B, H, N, d, dtype, seed=d + 3)
     out = ea.prefill(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale)
     torch.cuda.synchronize()
     rows = W.prefill_rows_sample(N, 16, seed=d)
-    for h in (0, H - 1):
+    for h in (0, 7, H - 1):
         ref = oracle.prefill_rows(f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1]), False, scale, 0, 0, rows)
-        check(f64(out[0, h, rows]), ref, "bf16", f"d={d} N=16384 h={h}")
+        check(f64(out[0, h, rows]), ref, dtype, f"d={d} {dtype} N=16384 h={h}")
     assert torch.isfinite(out).all()

@@ -42,9 +42,10 @@ def test_ragged_lengths(N, causal, d, dtype):
     full_parity(2, 3, N, d, dtype, causal, scale, seed=N)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("case", W.GPT2_F16, ids=lambda c: c.name)
-def test_gpt2_config(case):
-    full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed=0)
+def test_gpt2_config(case, seed):
+    full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed=seed)
 
 
 @pytest.mark.parametrize("case", [c for c in W.GPT2_SWEEP if c.N <= 1024], ids=lambda c: c.name)
@@ -52,11 +53,12 @@ def test_gpt2_sweep(case):
     full_parity(case.B, case.H, case.N, case.d, case.dtype, case.causal, case.scale, seed=1)
 
 
-def sampled_parity(case, seed, heads, nrows):
+def sampled_parity(case, seed, heads, nrows, early=0):
+    """Sampled rows (plus rows 1..early) of the given heads against the row oracle."""
     q, k, v = W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed)
     out = run(q, k, v, case.causal, case.scale)
     worst = 0.0
-    rows = W.prefill_rows_sample(case.N, nrows, seed)
+    rows = sorted(set(W.prefill_rows_sample(case.N, nrows, seed)) | set(range(1, min(case.N, early + 1))))
     for (b, h) in heads:
         # widen only the sampled head to fp64; the oracle reads just these rows of q
         ref = oracle.prefill_rows(f64(q[b, h])[None, None], f64(k[b, h])[None, None], f64(v[b, h])[None, None],
@@ -74,10 +76,14 @@ def test_dense_d128_sampled(case, seed):
     sampled_parity(case, seed, heads, nrows=48)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("case", W.LONG, ids=lambda c: c.name)
-def test_long_sampled(case):
+def test_long_sampled(case, seed):
+    """The long sequences (B=1, H=24, d=128, bf16: N=32768 full, N=16384 causal) at the
+    gate's three seeds.  Causal rows 1..16 average only a handful of values and carry
+    the thinnest bf16 margin, so they are always in the sample."""
     heads = [(0, 0), (0, 23), (0, 11)]
-    sampled_parity(case, 0, heads, nrows=32)
+    sampled_parity(case, seed, heads, nrows=32, early=16)
 
 
 @pytest.mark.parametrize("case", [c for c in W.GPT2_SWEEP if c.N == 4096], ids=lambda c: c.name)
