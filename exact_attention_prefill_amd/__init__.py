@@ -26,6 +26,7 @@ DECODE_ROW_GRANULE = 32
 DECODE_WGS_PER_CU = 8
 DECODE_MIN_CHUNK = 64
 DECODE_MFMA_LDS_BYTES = 163840
+DECODE_SCRATCH_BYTES = 16777216
 
 # Every symbol include/attn.h declares.
 EXPORTS = (
@@ -44,6 +45,7 @@ EXPORTS = (
     "attn_backward_workspace_bytes",
     "attn_prefill_plan",
     "attn_build_id",
+    "attn_decode_noalloc",
 )
 
 _lib = None
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_gqa_choose_split.restype = i
         L.attn_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
         L.attn_prefill_plan.restype = i
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        L.attn_decode_noalloc.restype = i
         L.attn_build_id.argtypes = []
         L.attn_build_id.restype = ctypes.c_char_p
         _lib = L
@@ -249,6 +253,28 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, out=None, 
         else:
             _check(lib().attn_decode_ex(pq, pk, pv, pl, po, B, H, max_len, d, dt, float(scale), int(chunk),
                                         wp or None, wb, st))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, out, scale: float | None = None, chunk: int = 0):
+    """attn_decode_noalloc: decode into ``out`` with the partials in the library's device
+    scratch array (no allocation by the library, none here: ``out`` is required).
+    Shapes as for decode; grouped K/V heads when k_cache has fewer heads than q."""
+    if q.dim() != 4 or q.shape[2] != 1 or k_cache.dim() != 4:
+        raise AttnValueError(ATTN_ERR_INVALID_ARG, "q must be (batch, heads, 1, d), caches (batch, heads, max_len, d)")
+    B, H, _, d = q.shape
+    Hkv, max_len = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    pq = _dev_tensor(q, "q", q.dtype, (B, H, 1, d))
+    pk = _dev_tensor(k_cache, "k_cache", q.dtype, (B, Hkv, max_len, d))
+    pv = _dev_tensor(v_cache, "v_cache", q.dtype, (B, Hkv, max_len, d))
+    pl = _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    po = _dev_tensor(out, "out", q.dtype, (B, H, 1, d))
+    with torch.cuda.device(q.device):
+        _check(lib().attn_decode_noalloc(pq, pk, pv, pl, po, B, H, Hkv, max_len, d, dt, float(scale), int(chunk),
+                                         _stream(q.device)))
     return out
 
 

@@ -257,7 +257,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d) {
 
 static int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                        int B, int H, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
-                       size_t ws_bytes, void* stream, bool caller_ws) {
+                       size_t ws_bytes, void* stream, bool caller_ws, bool use_scratch = false) {
   int st;
   if ((st = check_common(B, H, max_len, d, dtype, scale, "max_len")) != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
@@ -275,10 +275,23 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   if (caller_ws && !workspace && ws_bytes != 0) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but ws_bytes > 0");
 
   int n_split = 0;
+  if (use_scratch && chunk != 0 &&
+      attn_decode_workspace_bytes(B, H, (max_len + chunk - 1) / chunk, d) > (size_t)ATTN_DECODE_SCRATCH_BYTES)
+    return fail(ATTN_ERR_WORKSPACE, "the partials of chunk=%d (%zu bytes) exceed the %d-byte decode scratch", chunk,
+                attn_decode_workspace_bytes(B, H, (max_len + chunk - 1) / chunk, d), ATTN_DECODE_SCRATCH_BYTES);
+  if (use_scratch && attn_decode_workspace_bytes(B, H, 1, d) > (size_t)ATTN_DECODE_SCRATCH_BYTES)
+    return fail(ATTN_ERR_WORKSPACE, "B*H=%lld partials of d=%d exceed the %d-byte decode scratch even with one split",
+                (long long)B * H, d, ATTN_DECODE_SCRATCH_BYTES);
   if (chunk == 0) {
     int cus = 0;
     if ((st = device_cus(&cus)) != ATTN_OK) return st;
     if ((st = attn_decode_gqa_choose_split(B, H, Hkv, max_len, d, cus, &chunk, &n_split)) != ATTN_OK) return st;
+    // The scratch form takes the smallest legal chunk at or above the automatic one
+    // whose partials fit the scratch (one split always fits, checked above).
+    while (use_scratch && attn_decode_workspace_bytes(B, H, n_split, d) > (size_t)ATTN_DECODE_SCRATCH_BYTES) {
+      chunk += ATTN_DECODE_ROW_GRANULE;
+      n_split = (max_len + chunk - 1) / chunk;
+    }
   } else {
     n_split = (max_len + chunk - 1) / chunk;
   }
@@ -286,7 +299,12 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   bool own = false;
-  if (!caller_ws || (workspace == nullptr && ws_bytes == 0)) {
+  if (use_scratch) {
+    float* sp = nullptr;
+    hipError_t e = attn::decode_scratch(&sp);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode scratch lookup failed: %s", hipGetErrorString(e));
+    ws = sp;
+  } else if (!caller_ws || (workspace == nullptr && ws_bytes == 0)) {
     hipError_t e = hipMallocAsync(&ws, need, s);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace allocation of %zu bytes failed: %s", need, hipGetErrorString(e));
     own = true;
@@ -320,6 +338,12 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, con
                     size_t ws_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, max_len, d, dtype, scale, chunk, workspace,
                      ws_bytes, stream, true);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                        int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, max_len, d, dtype, scale, chunk, nullptr, 0,
+                     stream, false, true);
 }
 
 }  // extern "C"

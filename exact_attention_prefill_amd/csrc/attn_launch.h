@@ -24,6 +24,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
                          int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
                          hipStream_t st);
+// Device address of this device's decode scratch array (ATTN_DECODE_SCRATCH_BYTES),
+// looked up on the first call per device.
+hipError_t decode_scratch(float** ptr);
 int decode_heads_per_wave(int H, int Hkv);
 bool decode_uses_mfma(int H, int Hkv);
 int decode_mfma_waves_per_cu(int d);

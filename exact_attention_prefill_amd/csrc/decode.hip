@@ -20,6 +20,8 @@
 //   ml [(pair*n_split + s)*2 + 0, 1]      m = max_t c s_t, l = sum_t 2^(c s_t - m)
 // where acc is the first B*H*n_split*d floats and ml follows it.  A chunk at or past
 // the sequence's length writes only (m, l) = (-inf, 0); its acc is never read.
+#include <mutex>
+
 #include "attn.h"
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -606,6 +608,32 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
   ATTN_DEC(256)
 #undef ATTN_DEC
   return hipErrorInvalidValue;
+}
+
+// Partials of the allocation-free decode entry point: a fixed device array that the
+// code object carries, so a call needs no allocation.  Each device that loads the
+// library holds its own copy until the process ends.  Host code must never pass the
+// array's name to a kernel (on the host it is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, looked up once per device below.
+static __device__ __align__(256) char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+hipError_t decode_scratch(float** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = (float*)addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

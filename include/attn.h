@@ -174,6 +174,27 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, con
  * With Hkv == Hq it equals attn_decode_choose_split.  No HIP call. */
 int attn_decode_gqa_choose_split(int B, int Hq, int Hkv, int max_len, int d, int num_cus, int* chunk, int* n_split);
 
+/* Bytes of the device scratch array that holds attn_decode_noalloc's partials (16 MiB
+ * on every device the library runs on, held until the process ends). */
+#define ATTN_DECODE_SCRATCH_BYTES 16777216
+
+/* attn_decode_noalloc: attn_decode_gqa with no workspace and no allocation of any kind,
+ * for callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, and hosts that forbid allocation during a step.  The
+ * (m, l, acc) partials live in a fixed device array of ATTN_DECODE_SCRATCH_BYTES
+ * that the library carries, one per device.
+ *   Arguments, layout, validation and results as attn_decode_gqa (Hkv == Hq for
+ *   multi-head decode); chunk 0 selects the automatic chunk, raised to the smallest
+ *   legal chunk whose partials, attn_decode_workspace_bytes(B, Hq, n_split, d), fit the
+ *   scratch.  Given the same chunk, the output equals attn_decode_gqa's bit for bit.
+ *   Returns ATTN_ERR_WORKSPACE when an explicit chunk's partials exceed the scratch,
+ *   or when B*Hq*(d + 2)*4 bytes (one split per head) already does.
+ * Every call on a device shares that device's one array: calls that overlap in time
+ * on one device (other streams, other threads) race and must be serialised by the
+ * caller.  Each call overwrites every partial it reads, so nothing needs clearing. */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                        int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* stream);
+
 /* Backward pass (page 3, "Future work"): gradients of the loss sum(dout * out) for
  * out = attn_prefill_ex(q, k, v, causal, scale), given that call's out and lse.
  *   q, out, dout, dq : [B][Hq][N][d];  k, v, dk, dv : [B][Hkv][N][d] (Hkv divides Hq);

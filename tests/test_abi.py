@@ -263,3 +263,19 @@ def test_library_was_built_from_these_sources():
 
     assert ea.build_id() == build.source_hash()
 
+
+def test_noalloc_decode_validation():
+    """attn_decode_noalloc validates like attn_decode_gqa and refuses, before any HIP
+    call, an explicit chunk whose partials exceed the device scratch."""
+    L = ea.lib()
+    call = lambda B, H, Hkv, max_len, d, chunk: L.attn_decode_noalloc(  # noqa: E731
+        P[0], P[1], P[2], P[4], P[3], B, H, Hkv, max_len, d, 0, 0.125, chunk, None)
+    assert call(0, 1, 1, 64, 64, 0) == ea.ATTN_ERR_INVALID_ARG
+    assert call(1, 6, 4, 64, 64, 0) == ea.ATTN_ERR_INVALID_ARG  # Hkv does not divide H
+    assert call(1, 1, 1, 64, 80, 0) == ea.ATTN_ERR_UNSUPPORTED
+    assert call(1, 1, 1, 64, 64, 48) == ea.ATTN_ERR_INVALID_ARG  # not a multiple of the granule
+    assert ea.decode_workspace_bytes(64, 32, 128, 64) > ea.DECODE_SCRATCH_BYTES
+    assert call(64, 32, 32, 4096, 64, 32) == ea.ATTN_ERR_WORKSPACE
+    assert "scratch" in ea.last_error()
+    # One split per head already too large: B*H*(d+2)*4 bytes over the scratch.
+    assert call(64, 256, 256, 64, 256, 0) == ea.ATTN_ERR_WORKSPACE
