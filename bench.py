@@ -30,7 +30,9 @@ B, H and N (bf16, non-causal), outside the steps.
 each call; the calls small enough to be launch-bound also as one HIP graph of 20
 calls replayed, `graph_ms`, which leaves the host's launch overhead out): the small
 prefill (B=1, H=1, N=128, d=64, fp16), the GPT-2-like prompt (B=1, H=12, N=2048, d=64,
-fp16, full and causal), the dense d=128 token splits (B*N = 16384 at H=16), the long
+fp16, full and causal) and its sweep (B in {1, 4} x N in {128, 512, 1024, 4096}, both
+masks; `causal_speedup` is full time over causal time per shape), the dense d=128
+token splits (B*N = 16384 at H=16), the long
 sequences (B=1, H=24, d=128, bf16: N=32768 full, N=16384 causal) and the batch-1
 decode over a full 4096-row cache, cold like the step's decode.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same prefill; in
@@ -346,7 +348,7 @@ def main():
     # events: median of 10 launches after the clock has settled; decode cold as above.
     configs = {}
     if not args.no_configs:
-        for case in W.SMALL_F16 + W.GPT2_F16 + W.DENSE_D128 + W.LONG:
+        for case in W.SMALL_F16 + W.GPT2_F16 + W.GPT2_SWEEP + W.DENSE_D128 + W.LONG:
             cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(case.B, case.H, case.N, case.d, case.dtype, seed=0))
             cout = torch.empty_like(cq)
             ccall = lambda: ea.prefill(cq, ck, cv, causal=case.causal, scale=case.scale, out=cout)  # noqa: E731
@@ -358,6 +360,18 @@ def main():
                 gtf = case.flop / (gms * 1e-3) / 1e12
                 configs[case.name].update({"graph_ms": round(gms, 4), "graph_tflops": round(gtf, 1)})
             del cq, ck, cv, cout
+        # Causal tile skipping (page 3, "Kernel design" and "Performance": about 1.8-1.9x
+        # at N = 4096 on its GPU): full time over causal time per GPT-2-like shape, from
+        # the graph replays where the calls are launch-sized.
+        speedup = {}
+        for case in W.GPT2_F16 + W.GPT2_SWEEP:
+            if not case.causal:
+                continue
+            full = configs[case.name.replace("_causal", "_full")]
+            caus = configs[case.name]
+            key = "graph_ms" if "graph_ms" in full and "graph_ms" in caus else "ms"
+            speedup[case.name.replace("_causal", "")] = round(full[key] / caus[key], 3)
+        configs["causal_speedup"] = speedup
         D1 = W.DECODE[0]
         eq, ek, ev_, el = (t.to(dev) for t in W.decode_inputs(D1.B, D1.H, D1.max_len, D1.d, D1.dtype, seed=0))
         eout = torch.empty_like(eq)
@@ -372,7 +386,9 @@ def main():
         configs[D1.name] = {"us_cold": round(eus, 3), "gbs": round(egbs, 1), "frac": round(egbs / PEAK_HBM_GBS, 4),
                             "bytes": ebytes, "chunk": echunk, "n_split": ens}
         del eq, ek, ev_, eout, ews
-        log("configs: " + ", ".join(f"{k} {v.get('tflops', v.get('gbs'))}" for k, v in configs.items()))
+        log("configs: " + ", ".join(f"{k} {v.get('tflops', v.get('gbs'))}" for k, v in configs.items()
+                                    if k != "causal_speedup"))
+        log("causal speed-up (full / causal time): " + json.dumps(configs["causal_speedup"]))
 
     # The host leg: the fp64 CPU oracle, run only with the CPU baseline (it is skipped
     # with --no-cpu-baseline, as in every profiled run).  It checks this run's outputs

@@ -98,7 +98,7 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_gqa.restype = i
         L.attn_decode_gqa_choose_split.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.attn_decode_gqa_choose_split.restype = i
-        L.attn_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
+        L.attn_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 4
         L.attn_prefill_plan.restype = i
         L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
         L.attn_decode_noalloc.restype = i
@@ -295,11 +295,11 @@ def decode_gqa_choose_split(B: int, Hq: int, Hkv: int, max_len: int, d: int, num
 def prefill_plan(B: int, H: int, N: int, d: int, causal: bool, num_cus: int) -> dict:
     """The workgroup form attn_prefill takes for this shape on a device with num_cus CUs:
     {"waves": waves per workgroup, "rows_per_wave": query rows per wave, "stages": K/V
-    LDS stages}.  Host only."""
-    w, r, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    LDS stages, "key_groups": waves splitting each row block's keys}.  Host only."""
+    w, r, s, g = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     _check(lib().attn_prefill_plan(B, H, N, d, int(bool(causal)), num_cus, ctypes.byref(w), ctypes.byref(r),
-                                   ctypes.byref(s)))
-    return {"waves": w.value, "rows_per_wave": r.value, "stages": s.value}
+                                   ctypes.byref(s), ctypes.byref(g)))
+    return {"waves": w.value, "rows_per_wave": r.value, "stages": s.value, "key_groups": g.value}
 
 
 def decode_workspace_bytes(B: int, H: int, n_split: int, d: int) -> int:

@@ -138,17 +138,18 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* out, floa
 }
 
 int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* waves_per_workgroup,
-                      int* rows_per_wave, int* lds_stages) {
+                      int* rows_per_wave, int* lds_stages, int* key_groups) {
   if (B < 1 || H < 1 || N < 1 || num_cus < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H, N and num_cus must be >= 1");
   if (!head_dim_ok(d))
     return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d has no kernel (32, 64, 96, 128 or 256)", d);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
-  if (!waves_per_workgroup || !rows_per_wave || !lds_stages)
+  if (!waves_per_workgroup || !rows_per_wave || !lds_stages || !key_groups)
     return fail(ATTN_ERR_INVALID_ARG, "the plan outputs must be non-NULL host pointers");
   const attn::PrefillForm f = attn::prefill_form(B, H, N, d, causal, num_cus);
   *waves_per_workgroup = f.nw;
   *rows_per_wave = 32 * f.qb;
   *lds_stages = f.s4 ? 4 : 2;
+  *key_groups = f.kg;
   return ok();
 }
 

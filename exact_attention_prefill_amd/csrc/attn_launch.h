@@ -8,12 +8,13 @@
 namespace attn {
 
 // The workgroup form a prefill launch takes: waves per workgroup, 32-row query blocks
-// per wave, and whether K/V are staged in four LDS stages (one barrier per two tiles)
-// rather than two.
+// per wave, whether K/V are staged in four LDS stages (one barrier per two tiles)
+// rather than two, and the key groups that split each row block's keys between waves.
 struct PrefillForm {
   int nw;
   int qb;
   int s4;
+  int kg;
 };
 
 // The rule launch_prefill applies (host only; no HIP call).

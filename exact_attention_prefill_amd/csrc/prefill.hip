@@ -43,6 +43,7 @@ namespace prefill_cfg {
 [[maybe_unused]] constexpr int BN = 64;               // keys per tile
 [[maybe_unused]] constexpr float kLazyLog2 = 8.f;     // raise m only when a score exceeds it by > 2^8
 [[maybe_unused]] constexpr float kSumGuard = 4096.f;  // a unit's per-lane sum of p above this prompts a check
+[[maybe_unused]] constexpr float kMaxFloor = 1e30f;   // -m of a key-group row that has seen no visible key
 }  // namespace prefill_cfg
 
 struct PrefillParams {
@@ -79,14 +80,20 @@ constexpr int prefill_waves_per_simd() {
 // compiler's report that it cannot reach that occupancy is expected there.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wpass-failed"
-template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4>
+// KG > 1: key groups.  The NW waves form NW/KG row waves times KG key groups; the KG
+// waves of one row block sweep interleaved tiles (group g takes tiles g, g + KG, ...),
+// so a workgroup covers 32*QB*NW/KG query rows with KG times the waves on each, and the
+// groups' (m, l, acc) states meet in LDS at the end and are merged exactly (the decode
+// merge's rule, in a fixed order).  Staging then moves KG consecutive tiles per step.
+template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4, int KG>
 __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
   using namespace prefill_cfg;
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
   constexpr int QW = 32 * QB;                      // query rows per wave
-  constexpr int BM = QW * NW;                      // query rows per workgroup
+  constexpr int RW = NW / KG;                      // row waves (blocks of QW query rows)
+  constexpr int BM = QW * RW;                      // query rows per workgroup
   constexpr int RBG = D * 2;                       // bytes per K/V row in memory
   constexpr int RB = lds_row_bytes<D>();           // bytes per K/V row in LDS
   constexpr int CH = D / 8;                        // 16-byte chunks of a row that hold data
@@ -94,14 +101,17 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   constexpr int KS = D / 16;                       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;                       // 32-wide output blocks along d
   constexpr int TILE_BYTES = BN * RB;              // one K (or V) tile
-  constexpr int NLD = TILE_BYTES / 1024 / kWaves;  // 1 KiB LDS-direct loads per wave per tile
+  constexpr int STEP_BYTES = KG * TILE_BYTES;      // staged per step: KG consecutive tiles
+  constexpr int BNS = BN * KG;                     // keys per step
+  constexpr int NLD = STEP_BYTES / 1024 / kWaves;  // 1 KiB LDS-direct loads per wave per step
+  static_assert(KG == 1 || (!S4 && NW == 8), "key groups run on eight-wave, two-stage workgroups");
   static_assert(NLD >= 1, "tile too small for the load pattern");
   // Two K and two V tile buffers, each its own array so the compiler can tell the
   // in-flight LDS-direct loads into one from the operand reads of another.
-  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[STEP_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[STEP_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[STEP_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[STEP_BYTES];
   constexpr int XB = S4 ? TILE_BYTES : 16;  // the third and fourth stages (S4 only)
   __shared__ __attribute__((aligned(1024))) char kbuf2[XB];
   __shared__ __attribute__((aligned(1024))) char kbuf3[XB];
@@ -111,6 +121,8 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
+  const int kgrp = __builtin_amdgcn_readfirstlane(wave / RW);  // key group (0 when KG == 1)
+  const int rwave = wave - kgrp * RW;                          // row wave
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -145,7 +157,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   qb = __builtin_amdgcn_readfirstlane(qb);
   const int N = p.N;
   const int q0 = qb * BM;
-  const int qw0 = q0 + QW * wave;
+  const int qw0 = q0 + QW * rwave;
   int qrow[QB];
 #pragma unroll
   for (int cb = 0; cb < QB; ++cb) qrow[cb] = qw0 + 32 * cb + l32;
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   // chunk 2ks + half.
   uint32_t k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = l32 * RB + (((2 * ks + half) ^ kkey(l32)) << 4);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = kgrp * TILE_BYTES + l32 * RB + (((2 * ks + half) ^ kkey(l32)) << 4);
   // V^T operand via transpose loads: in each 16-lane group, source lane r points at
   // 4 consecutive d of key row (base + r/4), d0 = 32db + 16*((lane>>4)&1) + 4*(r&3);
   // base is a multiple of 8, so key(row) = key(row & 7).
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int chunk = 4 * db + 2 * gg + ((r & 3) >> 1);
-      v_off[db] = rowlo * RB + ((chunk ^ vkey(rowlo)) << 4) + 8 * (r & 1);
+      v_off[db] = kgrp * TILE_BYTES + rowlo * RB + ((chunk ^ vkey(rowlo)) << 4) + 8 * (r & 1);
     }
   }
 
@@ -229,15 +241,30 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kv_end + BN - 1) / BN;  // 64-key tiles this workgroup stages
-  const int nu = (kv_end + 31) / 32;      // 32-key units in those tiles
-  // Units this wave computes: a prefix (causal waves stop at their diagonal).
-  const int nu_w = qw0 >= N ? 0 : (CAUSAL ? min(nu, (qw0 + QW - 1) / 32 + 1) : nu);
+  const int nt = (kv_end + BNS - 1) / BNS;  // steps (KG 64-key tiles each) this workgroup stages
+  const int nu = (kv_end + 31) / 32;        // 32-key units in those tiles
+  // Units this wave computes: a prefix of its own units (causal waves stop at their
+  // diagonal).  With key groups a wave's units are the two halves of its tiles
+  // kgrp, kgrp + KG, ...: count those of them up to the last unit the rows need.
+  int nu_w;
+  if constexpr (KG == 1) {
+    nu_w = qw0 >= N ? 0 : (CAUSAL ? min(nu, (qw0 + QW - 1) / 32 + 1) : nu);
+  } else {
+    const int ulim = (CAUSAL ? min(nu, (qw0 + QW - 1) / 32 + 1) : nu) - 1;  // last unit needed
+    const int nfull = (ulim + 1) / 2;  // tiles whose two units are both needed
+    const int mine = nfull > kgrp ? (nfull - kgrp - 1) / KG + 1 : 0;
+    const bool half_tile = (ulim % 2 == 0) && ((ulim / 2) % KG == kgrp);
+    nu_w = qw0 >= N ? 0 : 2 * mine + (half_tile ? 1 : 0);
+  }
+  // First key of this wave's unit u.
+  auto unit_key0 = [&](int u) __attribute__((always_inline)) {
+    return KG == 1 ? 32 * u : BN * ((u >> 1) * KG + kgrp) + 32 * (u & 1);
+  };
 
-  if (N % BN != 0) {
+  if (N % BNS != 0) {
     // The last tile is partial and its missing rows are never written: start from
     // zeros so no uninitialised LDS bits can reach the MFMA (masked p is exactly 0).
-    for (int i = tid; i < TILE_BYTES / 16; i += kThreads) {
+    for (int i = tid; i < STEP_BYTES / 16; i += kThreads) {
       ((u32x4*)kbuf0)[i] = (u32x4){0, 0, 0, 0};
       ((u32x4*)kbuf1)[i] = (u32x4){0, 0, 0, 0};
       ((u32x4*)vbuf0)[i] = (u32x4){0, 0, 0, 0};
@@ -254,9 +281,9 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   }
 
   auto load_tile = [&](const char* src_base, const uint32_t (&offs)[NLD], int t, char* dst) __attribute__((always_inline)) {
-    const int k0 = t * BN;
+    const int k0 = t * BNS;
     const int rows_left = N - k0;
-    const uint32_t nrec = (uint32_t)(rows_left < BN ? rows_left : BN) * RBG;
+    const uint32_t nrec = (uint32_t)(rows_left < BNS ? rows_left : BNS) * RBG;
     // Buffer descriptor: base address, stride 0, nrec bytes in range (rows past the
     // end read nothing), raw dword format.
     const u32x4 r = buffer_rsrc(src_base + (size_t)k0 * RBG, nrec);
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   };
   // Keys past the end, and (causal) keys after the query row, score -inf.
   auto mask_unit = [&](f32x16& sc, int u, int cb) __attribute__((always_inline)) {
-    const int k0 = 32 * u;
+    const int k0 = unit_key0(u);
     const bool need = (k0 + 32 > N) || (CAUSAL && k0 + 31 > qw0 + 32 * cb);
     if (need) {
       const int lim = CAUSAL ? min(qrow[cb], N - 1) : N - 1;
@@ -457,7 +484,13 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) {
       mask_unit(sx[cb], 0, cb);
-      m_run[cb] = unit_max(sx[cb]) * p.c;  // key 0 is always visible, so this is finite
+      // Key 0 is visible to every row, so group 0's first max is finite.  The first tile
+      // of a later key group may hold no key a row can see: such a row starts from a
+      // finite floor instead of -inf, its p are 0 until a visible key arrives, whose p
+      // (2^(c s + kMaxFloor), an overflow) trips the sum guard and raises m to the
+      // row's real max with alpha = 0 (l and O are still 0 then).
+      m_run[cb] = unit_max(sx[cb]) * p.c;
+      if constexpr (KG > 1) m_run[cb] = fmaxf(m_run[cb], -kMaxFloor);
       neg_m[cb] = -m_run[cb];
       p_all(sx[cb], pa[cb], l_run[cb], neg_m[cb]);
     }
@@ -534,6 +567,61 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
     }
   }
 
+  if constexpr (KG > 1) {
+    // Key groups 1..KG-1 hand their states to group 0 of the same row block through the
+    // staging buffers, which every wave has finished reading; group 0 merges them in
+    // group order: M = max m, each state scaled by 2^(m_g - M) (a floor m gives 0).
+    // Both lanes of a row hold the same m, so the per-lane halves of l merge alike.
+    constexpr int RS = 64 * 4 * (QB * DB * 16 + 2 * QB);  // bytes of one wave's state
+    constexpr int PER = STEP_BYTES / RS;                   // states per staging buffer
+    static_assert(4 * PER >= (KG - 1) * RW, "the key groups' states do not fit the staging buffers");
+    auto region = [&](int g) __attribute__((always_inline)) {
+      const int r = (g - 1) * RW + rwave;
+      const int a = r / PER, o = (r - a * PER) * RS;
+      char* base = a == 0 ? kbuf0 : (a == 1 ? kbuf1 : (a == 2 ? vbuf0 : vbuf1));
+      return base + o;
+    };
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kgrp > 0) {
+      char* st = region(kgrp);
+#pragma unroll
+      for (int cb = 0; cb < QB; ++cb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            *(f32x4*)(st + (((cb * DB + db) * 4 + a) * 64 + lane) * 16) =
+                (f32x4){oacc[cb][db][4 * a], oacc[cb][db][4 * a + 1], oacc[cb][db][4 * a + 2], oacc[cb][db][4 * a + 3]};
+        *(float2*)(st + QB * DB * 16 * 64 * 4 + (cb * 64 + lane) * 8) = make_float2(m_run[cb], l_run[cb]);
+      }
+    }
+    __syncthreads();
+    if (kgrp == 0) {
+#pragma unroll
+      for (int g = 1; g < KG; ++g) {
+        const char* st = region(g);
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) {
+          const float2 ml = *(const float2*)(st + QB * DB * 16 * 64 * 4 + (cb * 64 + lane) * 8);
+          const float M = fmaxf(m_run[cb], ml.x);
+          const float a0 = fast_exp2(m_run[cb] - M), a1 = fast_exp2(ml.x - M);
+          m_run[cb] = M;
+          l_run[cb] = l_run[cb] * a0 + ml.y * a1;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const f32x4 o = *(const f32x4*)(st + (((cb * DB + db) * 4 + a) * 64 + lane) * 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) oacc[cb][db][4 * a + e] = oacc[cb][db][4 * a + e] * a0 + o[e] * a1;
+            }
+        }
+      }
+    }
+    if (kgrp != 0) return;
+  }
+
   // Epilogue: O = acc / l.  Lane holds d = 32db + 8a + 4*half + b for a, b in 0..3.
   // The row's scaled scores satisfy sum_j exp(scale s_j) = 2^m l for the reference m
   // the row settled on, whatever it is, so its log-sum-exp is (m + log2 l) ln 2.
@@ -560,12 +648,12 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
 }
 #pragma clang diagnostic pop
 
-template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4 = false>
+template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4 = false, int KG = 1>
 static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
-  constexpr int BM = 32 * QB * NW;
+  constexpr int BM = 32 * QB * NW / KG;
   p.nqblk = (p.N + BM - 1) / BM;
   const long long grid = (long long)p.nqblk * p.H * p.B;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL, NW, QB, S4>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL, NW, QB, S4, KG>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -599,8 +687,25 @@ static int short_workgroup_limit(int d, bool causal) {
 // d = 256 needs one SIMD per wave (its Q operands and O accumulators alone take
 // 192 registers) and 128 KiB of LDS per four-wave workgroup: four waves, one
 // workgroup per CU.
+// Small grids (at most one 128-row block per CU, causal at most two) leave CUs idle or
+// run one wave per SIMD; they take eight-wave workgroups whose waves split the keys
+// (KG key groups), so every SIMD holds two waves and a block's tiles are shared out:
+// 128-row blocks of two groups, or, at d <= 64 (whose four tiles per stage fit the
+// LDS), 64-row blocks of four groups when those fit one round on the CUs, or for causal
+// grids of long sequences (N >= 2048: the long diagonal blocks hold a quarter of their
+// tiles each; the short ones of a second round fill in behind them).  Measured against
+// the four-wave forms (graph replays, us): B=1 H=12 d=64 N=512 / 1024 / 2048 full 9.9 /
+// 15.8 / 27.3 -> 7.8 / 10.3 / 22.4, causal 9.7 / 15.7 / 27.5 -> 8.2 / 10.7 / 21.4;
+// causal N=4096 67.2 -> 47.8, d=128 H=16 N=1024 / 2048 / 4096 causal 23.5 / 41.7 / 87.9
+// -> 20.7 / 33.3 / 75.6; causal B=4 N=512 9.97 -> 10.23 and B=4 N=1024 17.5 -> 17.8
+// (four groups there, whose 64-row blocks take two short rounds, measured 13.1).
 PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
-  if (d > 128) return {4, 1, 0};
+  if (d > 128) return {4, 1, 0, 1};
+  const long long blocks4 = (long long)B * H * ((N + 127) / 128);
+  if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) {
+    if (d <= 64 && (2 * blocks4 <= num_cus || (causal && N >= 2048 && blocks4 <= num_cus))) return {8, 1, 0, 4};
+    return {8, 1, 0, 2};
+  }
   // Full grids take the eight-wave forms from two 256-row blocks per CU (+3-5% at
   // two to three per CU, d = 64 +13%); causal grids, whose workgroups vary in length,
   // from four (at three per CU they measured 3% slower on it).
@@ -610,8 +715,8 @@ PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
   // way) but pay only on the full d = 64 grids: +1.4-1.9% at B*H*N = 0.26M..0.79M
   // rows; d = 128 lost 3%, causal d = 64 4%, d = 96 up to 1%, d = 32 measured flat.
   if (blocks8 >= (causal ? 4LL : 2LL) * num_cus && !short_wgs) {
-    if (d == 64) return {8, 2, causal ? 0 : 1};
-    return {8, 1, 0};
+    if (d == 64) return {8, 2, causal ? 0 : 1, 1};
+    return {8, 1, 0, 1};
   }
   // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two
   // workgroups still share a CU): four stages for grids of at most two 128-row blocks
@@ -626,13 +731,12 @@ PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
   // causal grids of at most two (+8-13% at B = 1, H = 12..16, N = 4096).  Full grids
   // of two blocks per CU lost 23-36% on it (two rounds of workgroups), causal grids
   // of three to eight 14-40%.
-  const long long blocks4 = (long long)B * H * ((N + 127) / 128);
   if (d <= 64) {
-    if (blocks4 <= 2LL * num_cus || (d == 64 && causal)) return {4, 1, 1};
+    if (blocks4 <= 2LL * num_cus || (d == 64 && causal)) return {4, 1, 1, 1};
   } else {
-    if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) return {4, 1, 1};
+    if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) return {4, 1, 1, 1};
   }
-  return {4, 1, 0};
+  return {4, 1, 0, 1};
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -641,6 +745,10 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
   if constexpr (D > 128) {
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
+    if constexpr (D <= 64) {
+      if (f.kg == 4) return launch_prefill_t<DT, D, CAUSAL, 8, 1, false, 4>(p, s);
+    }
+    if (f.kg == 2) return launch_prefill_t<DT, D, CAUSAL, 8, 1, false, 2>(p, s);
     if (f.nw == 8) {
       if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2, !CAUSAL>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);

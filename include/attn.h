@@ -65,16 +65,20 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
 
 /* Host-only: the workgroup form attn_prefill / attn_prefill_gqa / attn_prefill_ex take
  * for this shape on a device with num_cus compute units (page 3, "Kernel design": the
- * work is cut into independent (query block, head, batch) pieces; the block height
- * follows the grid so that the device stays full).  Writes to HOST pointers:
+ * work is cut into independent (query block, head, batch) pieces sized so that the
+ * device stays full; "Challenges and debugging": a launch of too few blocks starves
+ * the GPU).  Writes to HOST pointers:
  *   waves_per_workgroup : 4 or 8 waves of 64 lanes;
- *   rows_per_wave       : query rows each wave owns (32 or 64), so one workgroup
- *                         covers waves_per_workgroup * rows_per_wave query rows;
- *   lds_stages          : K/V tiles held in on-chip memory per operand (2 or 4).
- * Every form computes each row with the same arithmetic.  Validation as for
- * attn_prefill (Hkv does not affect the form).  No HIP call. */
+ *   rows_per_wave       : query rows each wave owns (32 or 64);
+ *   lds_stages          : K/V tiles held in on-chip memory per operand (2 or 4);
+ *   key_groups          : 1, or 2 or 4 when the waves of each row block split its keys
+ *                         (small grids); a workgroup covers
+ *                         waves_per_workgroup * rows_per_wave / key_groups query rows.
+ * Forms with one key group compute each row with the same arithmetic (bit-identical
+ * rows); key groups sum a row's keys in another order, within the same tolerance.
+ * Validation as for attn_prefill (Hkv does not affect the form).  No HIP call. */
 int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* waves_per_workgroup,
-                      int* rows_per_wave, int* lds_stages);
+                      int* rows_per_wave, int* lds_stages, int* key_groups);
 
 /* Decode (page 3, "What can it do": generation phase; "Installation": decode(q,
  * k_cache, v_cache, seq_lens, scale)).

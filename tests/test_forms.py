@@ -17,7 +17,7 @@ def reachable_forms():
     found = set()
     for d, causal, bh, n in itertools.product((32, 64, 96, 128, 256), (False, True), bhs, ns):
         p = ea.prefill_plan(1, bh, n, d, causal, CUS)
-        found.add((d, causal, (p["waves"], p["rows_per_wave"], p["stages"])))
+        found.add((d, causal, (p["waves"], p["rows_per_wave"], p["stages"], p["key_groups"])))
     return found
 
 
@@ -35,10 +35,16 @@ def test_cases_reach_every_form():
 def test_rule_boundaries():
     # The headline shape (B=1, H=16, N=16384, d=128, full) runs eight waves of one
     # 32-row block each, two stages; d = 64 there runs two blocks per wave.
-    assert ea.prefill_plan(1, 16, 16384, 128, False, 256) == {"waves": 8, "rows_per_wave": 32, "stages": 2}
-    assert ea.prefill_plan(1, 16, 16384, 64, False, 256) == {"waves": 8, "rows_per_wave": 64, "stages": 4}
-    # The GPT-2-like prompt (192 four-wave workgroups on 256 CUs).
-    assert ea.prefill_plan(1, 12, 2048, 64, False, 256)["waves"] == 4
-    # d = 256 always runs four waves, two stages.
+    P = lambda *a: ea.prefill_plan(*a)  # noqa: E731
+    assert P(1, 16, 16384, 128, False, 256) == {"waves": 8, "rows_per_wave": 32, "stages": 2, "key_groups": 1}
+    assert P(1, 16, 16384, 64, False, 256) == {"waves": 8, "rows_per_wave": 64, "stages": 4, "key_groups": 1}
+    # The GPT-2-like prompt (B=1, H=12, N=2048, d=64: 192 128-row blocks on 256 CUs) splits
+    # each block's keys: two groups full, four causal (64-row blocks).
+    assert P(1, 12, 2048, 64, False, 256) == {"waves": 8, "rows_per_wave": 32, "stages": 2, "key_groups": 2}
+    assert P(1, 12, 2048, 64, True, 256) == {"waves": 8, "rows_per_wave": 32, "stages": 2, "key_groups": 4}
+    # Key groups stop above one 128-row block per CU.
+    assert P(1, 2, 128 * 128, 128, False, 256)["key_groups"] == 2
+    assert P(1, 2, 128 * 128 + 1, 128, False, 256)["key_groups"] == 1
+    # d = 256 always runs four waves, two stages, one key group.
     for n in (1, 5000, 40000):
-        assert ea.prefill_plan(1, 64, n, 256, True, 256) == {"waves": 4, "rows_per_wave": 32, "stages": 2}
+        assert P(1, 64, n, 256, True, 256) == {"waves": 4, "rows_per_wave": 32, "stages": 2, "key_groups": 1}

@@ -9,8 +9,9 @@ A second set draws small grids, of B*H*ceil(N/128) blocks around one and two per
 where the number of LDS stages changes (four on small grids, by head size and mask).
 
 Every case is checked on sampled rows against the fp64 oracle, and whole heads are
-compared bit for bit with one-head calls (a one-head grid always takes the four-wave,
-one-block form, and a row's arithmetic does not depend on the form).
+compared with the same heads from a call of another form (a slice of whole K/V groups):
+bit for bit when both forms have one key group (a row's arithmetic does not depend on
+such a form), within the gate when either splits the keys between waves.
 """
 
 import numpy as np
@@ -20,7 +21,7 @@ import torch
 import exact_attention_prefill_amd as ea
 import oracle
 import workloads as W
-from parity import check, f64
+from parity import check, f64, one_group_heads, plan_form, same_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -84,12 +85,22 @@ def test_random_shape(case):
     assert torch.isfinite(out).all()
     rows = W.prefill_rows_sample(N, 24, seed=i)
     g = H // Hkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    form = plan_form(B, H, N, d, causal, cus)
+    # Reference: the head inside a slice of whole K/V groups that runs another form with
+    # one key group (bit-identical rows when this form has one key group too), else the
+    # head's own group alone.
+    kk = one_group_heads(H // g, N, d, causal, cus, avoid=form)
+    ng = kk if kk is not None else 1
+    ref_form = plan_form(1, ng * g, N, d, causal, cus)
     for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 2)):
         kvh = h // g
-        single = ea.prefill(qd[b:b + 1, h:h + 1].contiguous(), kd[b:b + 1, kvh:kvh + 1].contiguous(),
-                            vd[b:b + 1, kvh:kvh + 1].contiguous(), causal=causal, scale=scale)
+        k0 = min(kvh, H // g - ng)
+        single = ea.prefill(qd[b:b + 1, k0 * g:(k0 + ng) * g].contiguous(), kd[b:b + 1, k0:k0 + ng].contiguous(),
+                            vd[b:b + 1, k0:k0 + ng].contiguous(), causal=causal, scale=scale)
         torch.cuda.synchronize()
-        assert torch.equal(out[b, h].view(torch.int16), single[0, 0].view(torch.int16)), (b, h)
+        same_rows(out[b, h], single[0, h - k0 * g], form, ref_form, dtype, f"case {case} b={b} h={h}")
         ref = oracle.prefill_rows(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, kvh:kvh + 1]),
                                   f64(v[b:b + 1, kvh:kvh + 1]), causal, scale, 0, 0, rows)
         check(f64(out[b, h, rows]), ref, dtype, f"case {case} b={b} h={h}")
+        check(f64(single[0, h - k0 * g, rows]), ref, dtype, f"case {case} b={b} h={h} reference form")

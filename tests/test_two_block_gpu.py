@@ -6,8 +6,10 @@ causal: N > 12288) run d = 64 with eight-wave, 512-row workgroups in which every
 owns two 32-row blocks and reads each K and V operand once for both (full grids keep
 four K/V tiles in LDS, causal ones two).  The shapes below reach that form with ragged lengths; smaller
 grids (one head at a time) run one block per wave.  A row's arithmetic does not depend
-on the workgroup form, so every row of the large call must equal the one-head call bit
-for bit; sampled rows are also checked against the oracle.
+on the workgroup form (among forms with one key group), so every row of the large call
+must equal the same head from a call on a slice of the heads (four-wave workgroups)
+bit for bit;
+sampled rows are also checked against the oracle.
 """
 
 import numpy as np
@@ -17,7 +19,7 @@ import torch
 import exact_attention_prefill_amd as ea
 import oracle
 import workloads as W
-from parity import check, f64
+from parity import check, f64, one_group_heads, plan_form
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,8 +40,21 @@ def reaches_two_block_form(case):
 
 
 def one_head(q, k, v, b, h, causal, scale, lse=False):
-    sl = lambda t: t[b:b + 1, h:h + 1].contiguous()  # noqa: E731
-    return ea.prefill(sl(q), sl(k), sl(v), causal=causal, scale=scale, lse=lse)
+    """Head (b, h) computed in a call of another form: the smallest slice of heads holding
+    it that runs four-wave workgroups of one 32-row block per wave and one key group.
+    Returns that head alone, shaped (1, 1, N, d)."""
+    H, N, d = q.shape[1], q.shape[2], q.shape[3]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = one_group_heads(H, N, d, causal, cus)
+    assert n is not None
+    f = plan_form(1, n, N, d, causal, cus)
+    assert f[0] == 4 and f[1] == 32 and f[3] == 1, f
+    h0 = min(h, H - n)
+    sl = lambda t: t[b:b + 1, h0:h0 + n].contiguous()  # noqa: E731
+    r = ea.prefill(sl(q), sl(k), sl(v), causal=causal, scale=scale, lse=lse)
+    if lse:
+        return r[0][:, h - h0:h - h0 + 1], r[1][:, h - h0:h - h0 + 1]
+    return r[:, h - h0:h - h0 + 1]
 
 
 def grow_keys(k, N):
