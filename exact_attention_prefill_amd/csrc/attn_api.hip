@@ -148,7 +148,7 @@ int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* 
   const attn::PrefillForm f = attn::prefill_form(B, H, N, d, causal, num_cus);
   *waves_per_workgroup = f.nw;
   *rows_per_wave = 32 * f.qb;
-  *lds_stages = f.s4 ? 4 : 2;
+  *lds_stages = f.st;
   *key_groups = f.kg;
   return ok();
 }

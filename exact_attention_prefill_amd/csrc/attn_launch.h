@@ -8,12 +8,12 @@
 namespace attn {
 
 // The workgroup form a prefill launch takes: waves per workgroup, 32-row query blocks
-// per wave, whether K/V are staged in four LDS stages (one barrier per two tiles)
-// rather than two, and the key groups that split each row block's keys between waves.
+// per wave, K/V tiles staged in LDS per operand (2, or 4 with one barrier per two
+// tiles), and the key groups that split each row block's keys between waves.
 struct PrefillForm {
   int nw;
   int qb;
-  int s4;
+  int st;
   int kg;
 };
 

@@ -85,7 +85,7 @@ constexpr int prefill_waves_per_simd() {
 // so a workgroup covers 32*QB*NW/KG query rows with KG times the waves on each, and the
 // groups' (m, l, acc) states meet in LDS at the end and are merged exactly (the decode
 // merge's rule, in a fixed order).  Staging then moves KG consecutive tiles per step.
-template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4, int KG>
+template <int DT, int D, bool CAUSAL, int NW, int QB, int ST, int KG>
 __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void prefill_kernel(PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses gfx950-only types; the host pass needs only the stub
   using namespace prefill_cfg;
@@ -104,7 +104,9 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   constexpr int STEP_BYTES = KG * TILE_BYTES;      // staged per step: KG consecutive tiles
   constexpr int BNS = BN * KG;                     // keys per step
   constexpr int NLD = STEP_BYTES / 1024 / kWaves;  // 1 KiB LDS-direct loads per wave per step
-  static_assert(KG == 1 || (!S4 && NW == 8), "key groups run on eight-wave, two-stage workgroups");
+  constexpr bool S4 = ST == 4;  // four stages, one barrier per two tiles
+  static_assert(ST == 2 || ST == 4, "two or four K/V stages");
+  static_assert(KG == 1 || (ST == 2 && NW == 8), "key groups run on eight-wave, two-stage workgroups");
   static_assert(NLD >= 1, "tile too small for the load pattern");
   // Two K and two V tile buffers, each its own array so the compiler can tell the
   // in-flight LDS-direct loads into one from the operand reads of another.
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   __shared__ __attribute__((aligned(1024))) char kbuf1[STEP_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[STEP_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf1[STEP_BYTES];
-  constexpr int XB = S4 ? TILE_BYTES : 16;  // the third and fourth stages (S4 only)
+  constexpr int XB = S4 ? TILE_BYTES : 16;  // the third and fourth stages (four stages only)
   __shared__ __attribute__((aligned(1024))) char kbuf2[XB];
   __shared__ __attribute__((aligned(1024))) char kbuf3[XB];
   __shared__ __attribute__((aligned(1024))) char vbuf2[XB];
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   auto mask_unit = [&](f32x16& sc, int u, int cb) __attribute__((always_inline)) {
     const int k0 = unit_key0(u);
     const bool need = (k0 + 32 > N) || (CAUSAL && k0 + 31 > qw0 + 32 * cb);
-    if (need) {
+    if (__builtin_expect(need, 0)) {  // rare: tail and diagonal units only
       const int lim = CAUSAL ? min(qrow[cb], N - 1) : N - 1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
       p_pack((7 & 1) ? xb[cb] : xa[cb], pnext[cb], l_unit[cb], 7);
       over = over || (l_unit[cb] > kSumGuard);
     }
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {  // rare: laid out off the hot path
 #pragma unroll
       for (int cb = 0; cb < QB; ++cb) {
         const bool row_over = xhalf_max(l_unit[cb]) > kSumGuard;  // this row's own guard
@@ -648,12 +650,12 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
 }
 #pragma clang diagnostic pop
 
-template <int DT, int D, bool CAUSAL, int NW, int QB, bool S4 = false, int KG = 1>
+template <int DT, int D, bool CAUSAL, int NW, int QB, int ST = 2, int KG = 1>
 static hipError_t launch_prefill_t(PrefillParams p, hipStream_t s) {
   constexpr int BM = 32 * QB * NW / KG;
   p.nqblk = (p.N + BM - 1) / BM;
   const long long grid = (long long)p.nqblk * p.H * p.B;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL, NW, QB, S4, KG>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, CAUSAL, NW, QB, ST, KG>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -700,11 +702,11 @@ static int short_workgroup_limit(int d, bool causal) {
 // -> 20.7 / 33.3 / 75.6; causal B=4 N=512 9.97 -> 10.23 and B=4 N=1024 17.5 -> 17.8
 // (four groups there, whose 64-row blocks take two short rounds, measured 13.1).
 PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
-  if (d > 128) return {4, 1, 0, 1};
+  if (d > 128) return {4, 1, 2, 1};
   const long long blocks4 = (long long)B * H * ((N + 127) / 128);
   if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) {
-    if (d <= 64 && (2 * blocks4 <= num_cus || (causal && N >= 2048 && blocks4 <= num_cus))) return {8, 1, 0, 4};
-    return {8, 1, 0, 2};
+    if (d <= 64 && (2 * blocks4 <= num_cus || (causal && N >= 2048 && blocks4 <= num_cus))) return {8, 1, 2, 4};
+    return {8, 1, 2, 2};
   }
   // Full grids take the eight-wave forms from two 256-row blocks per CU (+3-5% at
   // two to three per CU, d = 64 +13%); causal grids, whose workgroups vary in length,
@@ -715,8 +717,8 @@ PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
   // way) but pay only on the full d = 64 grids: +1.4-1.9% at B*H*N = 0.26M..0.79M
   // rows; d = 128 lost 3%, causal d = 64 4%, d = 96 up to 1%, d = 32 measured flat.
   if (blocks8 >= (causal ? 4LL : 2LL) * num_cus && !short_wgs) {
-    if (d == 64) return {8, 2, causal ? 0 : 1, 1};
-    return {8, 1, 0, 1};
+    if (d == 64) return {8, 2, causal ? 2 : 4, 1};
+    return {8, 1, 2, 1};
   }
   // d = 32 and 64 on the four-wave form (64 KiB of LDS for four stages, so two
   // workgroups still share a CU): four stages for grids of at most two 128-row blocks
@@ -732,11 +734,11 @@ PrefillForm prefill_form(int B, int H, int N, int d, int causal, int num_cus) {
   // of two blocks per CU lost 23-36% on it (two rounds of workgroups), causal grids
   // of three to eight 14-40%.
   if (d <= 64) {
-    if (blocks4 <= 2LL * num_cus || (d == 64 && causal)) return {4, 1, 1, 1};
+    if (blocks4 <= 2LL * num_cus || (d == 64 && causal)) return {4, 1, 4, 1};
   } else {
-    if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) return {4, 1, 1, 1};
+    if (blocks4 <= (causal ? 2LL : 1LL) * num_cus) return {4, 1, 4, 1};
   }
-  return {4, 1, 0, 1};
+  return {4, 1, 2, 1};
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -746,14 +748,14 @@ static hipError_t launch_prefill_w(const PrefillParams& p, int num_cus, hipStrea
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   } else {
     if constexpr (D <= 64) {
-      if (f.kg == 4) return launch_prefill_t<DT, D, CAUSAL, 8, 1, false, 4>(p, s);
+      if (f.kg == 4) return launch_prefill_t<DT, D, CAUSAL, 8, 1, 2, 4>(p, s);
     }
-    if (f.kg == 2) return launch_prefill_t<DT, D, CAUSAL, 8, 1, false, 2>(p, s);
+    if (f.kg == 2) return launch_prefill_t<DT, D, CAUSAL, 8, 1, 2, 2>(p, s);
     if (f.nw == 8) {
-      if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2, !CAUSAL>(p, s);
+      if constexpr (D == 64) return launch_prefill_t<DT, D, CAUSAL, 8, 2, CAUSAL ? 2 : 4>(p, s);
       else return launch_prefill_t<DT, D, CAUSAL, 8, 1>(p, s);
     }
-    if (f.s4) return launch_prefill_t<DT, D, CAUSAL, 4, 1, true>(p, s);
+    if (f.st == 4) return launch_prefill_t<DT, D, CAUSAL, 4, 1, 4>(p, s);
     return launch_prefill_t<DT, D, CAUSAL, 4, 1>(p, s);
   }
 }
