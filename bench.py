@@ -17,6 +17,9 @@ Prints ONE JSON line.  `value` is prefill TFLOP/s over the whole timed region
 time).  `roofline` covers the prefill kernel, timed with HIP events on the stream it
 runs on.  `decode` reports the decode path's HBM rate, timed with events after a
 512 MiB read that evicts the L2 and the Infinity Cache before every call.
+It also times the two passes apart (`split_us_cold`, `merge_us`: events at the
+boundaries of attn_decode_split and attn_decode_merge) and, as the floor the split pass
+is measured against, a plain cold read of the same bytes (`read_floor`).
 `decode_gqa` does the same for grouped K/V heads (B=8, 32 query heads over 8 K/V
 heads of 128, bf16, cache 4096 rows), whose bytes count the cache once per K/V head;
 it runs after the timed steps and is not part of them.
@@ -244,6 +247,35 @@ def main():
     dec_gbs = dec_bytes / (cold_us * 1e-6) / 1e9
     log(f"decode cold {cold_us:.2f} us = {dec_gbs:.0f} GB/s; warm {warm_us:.2f} us")
 
+    # The two passes apart (attn_decode_split, then attn_decode_merge on the partials it
+    # left), cold as above; and the floor the split pass is measured against: a plain cold
+    # read of the same bytes by as many waves as the split has non-empty chunks, each
+    # reading one contiguous span (attn_measure_read).
+    def passes_cold(iters):
+        spans = []
+        for _ in range(iters):
+            torch.sum(flush, dim=0, out=flush_sink)
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record()
+            ea.decode_split(dq_, dk_, dv_, dl_, D.scale, chunk, ws)
+            b.record()
+            ea.decode_merge(ws, dout, D.max_len, chunk)
+            c.record()
+            spans.append((a, b, c))
+        torch.cuda.synchronize()
+        return (float(np.mean([a.elapsed_time(b) for a, b, _ in spans])) * 1e3,
+                float(np.mean([b.elapsed_time(c) for _, b, c in spans])) * 1e3)
+
+    split_us, merge_us = passes_cold(args.decode_iters)
+    live_waves = D.H * sum(-(-int(L) // chunk) for L in dl.tolist())
+    read_buf = torch.empty((dec_bytes + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    read_sink = torch.zeros(live_waves * 64, dtype=torch.int32, device=dev)
+    read_us = cold_us_of(lambda: ea.measure_read(read_buf, live_waves, read_sink), args.decode_iters)
+    del read_buf
+    log(f"decode passes cold: split {split_us:.2f} us, merge {merge_us:.2f} us (events at the pass boundaries); "
+        f"plain read of the same bytes by {live_waves} waves {read_us:.2f} us = "
+        f"{dec_bytes / (read_us * 1e-6) / 1e9:.0f} GB/s")
+
     # Grouped K/V heads (a wider row than the step: the K/V cache is read once per
     # group of query heads), timed the same way outside the step.
     GQ = W.DECODE_GQA[0]
@@ -467,6 +499,12 @@ def main():
             "us_cold": round(cold_us, 3),
             "us_warm": round(warm_us, 3),
             "bytes": dec_bytes,
+            "split_us_cold": round(split_us, 3),
+            "merge_us": round(merge_us, 3),
+            "read_floor": {"us_cold": round(read_us, 3), "waves": live_waves,
+                           "gbs": round(dec_bytes / (read_us * 1e-6) / 1e9, 1),
+                           "what": "attn_measure_read of the same bytes, one contiguous span per wave, as many "
+                                   "waves as the split pass has non-empty chunks"},
         },
         "decode_gqa": {
             "bound": "hbm",

@@ -46,6 +46,9 @@ EXPORTS = (
     "attn_prefill_plan",
     "attn_build_id",
     "attn_decode_noalloc",
+    "attn_decode_split",
+    "attn_decode_merge",
+    "attn_measure_read",
 )
 
 _lib = None
@@ -102,6 +105,12 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_plan.restype = i
         L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
         L.attn_decode_noalloc.restype = i
+        L.attn_decode_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_decode_split.restype = i
+        L.attn_decode_merge.argtypes = [vp, sz, vp, i, i, i, i, i, i, vp]
+        L.attn_decode_merge.restype = i
+        L.attn_measure_read.argtypes = [vp, sz, i, vp, sz, vp]
+        L.attn_measure_read.restype = i
         L.attn_build_id.argtypes = []
         L.attn_build_id.restype = ctypes.c_char_p
         _lib = L
@@ -276,6 +285,40 @@ def decode_noalloc(q, k_cache, v_cache, seq_lens, out, scale: float | None = Non
         _check(lib().attn_decode_noalloc(pq, pk, pv, pl, po, B, H, Hkv, max_len, d, dt, float(scale), int(chunk),
                                          _stream(q.device)))
     return out
+
+
+def decode_split(q, k_cache, v_cache, seq_lens, scale, chunk: int, workspace):
+    """attn_decode_split: the split pass alone; leaves the (m, l, acc) partials in
+    ``workspace`` (a GPU tensor of at least decode_workspace_bytes bytes)."""
+    B, H, _, d = q.shape
+    Hkv, max_len = k_cache.shape[1], k_cache.shape[2]
+    pq = _dev_tensor(q, "q", q.dtype, (B, H, 1, d))
+    pk = _dev_tensor(k_cache, "k_cache", q.dtype, (B, Hkv, max_len, d))
+    pv = _dev_tensor(v_cache, "v_cache", q.dtype, (B, Hkv, max_len, d))
+    pl = _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    with torch.cuda.device(q.device):
+        _check(lib().attn_decode_split(pq, pk, pv, pl, B, H, Hkv, max_len, d, _dtype_code(q), float(scale), int(chunk),
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(q.device)))
+
+
+def decode_merge(workspace, out, max_len: int, chunk: int):
+    """attn_decode_merge: the merge pass alone, from the partials decode_split left in
+    ``workspace``, into ``out`` (B, H, 1, d)."""
+    B, H, _, d = out.shape
+    po = _dev_tensor(out, "out", out.dtype, (B, H, 1, d))
+    with torch.cuda.device(out.device):
+        _check(lib().attn_decode_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), po, B, H,
+                                       max_len, d, _dtype_code(out), int(chunk), _stream(out.device)))
+    return out
+
+
+def measure_read(buf, waves: int, sink):
+    """attn_measure_read: a plain streaming read of the GPU tensor ``buf`` by ``waves``
+    single-wave workgroups (measurement only); ``sink`` a GPU tensor of waves * 256 bytes."""
+    with torch.cuda.device(buf.device):
+        _check(lib().attn_measure_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(waves), sink.data_ptr(),
+                                       sink.numel() * sink.element_size(), _stream(buf.device)))
 
 
 def decode_choose_split(B: int, H: int, max_len: int, d: int, num_cus: int):

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "bwd.hip", "measure.hip"]
 HEADERS = [os.path.join(CSRC, "attn_device.h"), os.path.join(CSRC, "attn_launch.h"), os.path.join(ROOT, "include", "attn.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

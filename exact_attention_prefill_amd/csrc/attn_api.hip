@@ -258,13 +258,15 @@ size_t attn_decode_workspace_bytes(int B, int H, int n_split, int d) {
 
 static int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                        int B, int H, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
-                       size_t ws_bytes, void* stream, bool caller_ws, bool use_scratch = false) {
+                       size_t ws_bytes, void* stream, bool caller_ws, bool use_scratch = false,
+                       int passes = attn::kDecodeSplitPass | attn::kDecodeMergePass) {
   int st;
   if ((st = check_common(B, H, max_len, d, dtype, scale, "max_len")) != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
-      (st = check_ptr(out, "out")))
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")))
     return st;
+  // The split pass alone writes no output.
+  if ((passes & attn::kDecodeMergePass) && (st = check_ptr(out, "out"))) return st;
   if (!seq_lens) return fail(ATTN_ERR_INVALID_ARG, "seq_lens is NULL");
   if (((uintptr_t)seq_lens & 3u) != 0) return fail(ATTN_ERR_ALIGNMENT, "seq_lens is not 4-byte aligned");
   if (out == q || out == k_cache || out == v_cache) return fail(ATTN_ERR_INVALID_ARG, "out must not alias an input");
@@ -313,7 +315,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
   }
   hipError_t e = attn::launch_decode(q, k_cache, v_cache, seq_lens, out, B, H, Hkv, max_len, d, dtype, scale, chunk,
-                                     n_split, (float*)ws, s);
+                                     n_split, (float*)ws, s, passes);
   if (own) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;
@@ -345,6 +347,47 @@ int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
                         int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* stream) {
   return decode_impl(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, max_len, d, dtype, scale, chunk, nullptr, 0,
                      stream, false, true);
+}
+
+int attn_decode_split(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, int B, int Hq,
+                      int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (chunk == 0) return fail(ATTN_ERR_INVALID_ARG, "the split pass needs an explicit chunk");
+  if (!workspace) return fail(ATTN_ERR_INVALID_ARG, "the split pass needs a workspace");
+  return decode_impl(q, k_cache, v_cache, seq_lens, nullptr, B, Hq, Hkv, max_len, d, dtype, scale, chunk, workspace,
+                     ws_bytes, stream, true, false, attn::kDecodeSplitPass);
+}
+
+int attn_decode_merge(const void* workspace, size_t ws_bytes, void* out, int B, int Hq, int max_len, int d, int dtype,
+                      int chunk, void* stream) {
+  int st;
+  if ((st = check_common(B, Hq, max_len, d, dtype, 1.f, "max_len")) != ATTN_OK) return st;
+  if ((st = check_ptr(out, "out")) || (st = check_ptr(workspace, "workspace"))) return st;
+  if (out == workspace) return fail(ATTN_ERR_INVALID_ARG, "out must not alias the workspace");
+  const int T = ATTN_DECODE_ROW_GRANULE;
+  const int cap = (max_len + T - 1) / T * T;
+  if (chunk < T || chunk % T != 0 || chunk > cap)
+    return fail(ATTN_ERR_INVALID_ARG, "chunk=%d must be a multiple of %d in [%d, %d]", chunk, T, T, cap);
+  const int n_split = (max_len + chunk - 1) / chunk;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, n_split, d);
+  if (ws_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  hipError_t e = attn::launch_decode(nullptr, nullptr, nullptr, nullptr, out, B, Hq, Hq, max_len, d, dtype, 1.f, chunk,
+                                     n_split, (float*)workspace, (hipStream_t)stream, attn::kDecodeMergePass);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_measure_read(const void* buf, size_t bytes, int waves, void* sink, size_t sink_bytes, void* stream) {
+  if (!buf || !sink) return fail(ATTN_ERR_INVALID_ARG, "buf and sink must be non-NULL");
+  if (!aligned16(buf)) return fail(ATTN_ERR_ALIGNMENT, "buf is not 16-byte aligned");
+  if (((uintptr_t)sink & 3u) != 0) return fail(ATTN_ERR_ALIGNMENT, "sink is not 4-byte aligned");
+  if (bytes < 16 || bytes % 16 != 0) return fail(ATTN_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (waves < 1 || (size_t)waves > bytes / 16) return fail(ATTN_ERR_INVALID_ARG, "waves=%d must lie in [1, bytes/16]", waves);
+  if (sink_bytes < (size_t)waves * 256)
+    return fail(ATTN_ERR_WORKSPACE, "sink of %zu bytes is smaller than the %zu needed", sink_bytes, (size_t)waves * 256);
+  hipError_t e = attn::launch_measure_read(buf, bytes, waves, (uint32_t*)sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "read launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

@@ -522,36 +522,41 @@ static hipError_t launch_merge(const DecodeParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// `passes`: kDecodeSplitPass and/or kDecodeMergePass.
 template <int DT, int D, int G>
-static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(p.n_split, p.H / G, p.B), dim3(64), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_merge<DT, D>(p, st);
+static hipError_t launch_decode_t(const DecodeParams& p, int passes, hipStream_t st) {
+  if (passes & kDecodeSplitPass) {
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(p.n_split, p.H / G, p.B), dim3(64), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return (passes & kDecodeMergePass) ? launch_merge<DT, D>(p, st) : hipSuccess;
 }
 
 bool decode_uses_mfma(int H, int Hkv);
 
 template <int DT, int D>
-static hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_mfma_kernel<DT, D>), dim3(p.n_split, p.Hkv, p.B), dim3(64), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_merge<DT, D>(p, st);
+static hipError_t launch_decode_mfma(const DecodeParams& p, int passes, hipStream_t st) {
+  if (passes & kDecodeSplitPass) {
+    hipLaunchKernelGGL((decode_split_mfma_kernel<DT, D>), dim3(p.n_split, p.Hkv, p.B), dim3(64), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return (passes & kDecodeMergePass) ? launch_merge<DT, D>(p, st) : hipSuccess;
 }
 
 template <int DT, int D>
-static hipError_t launch_decode_g(const DecodeParams& p, int G, hipStream_t st) {
-  if (decode_uses_mfma(p.H, p.Hkv)) return launch_decode_mfma<DT, D>(p, st);
+static hipError_t launch_decode_g(const DecodeParams& p, int G, int passes, hipStream_t st) {
+  if (decode_uses_mfma(p.H, p.Hkv)) return launch_decode_mfma<DT, D>(p, passes, st);
   switch (G) {
-    case 1: return launch_decode_t<DT, D, 1>(p, st);
-    case 2: return launch_decode_t<DT, D, 2>(p, st);
-    case 3: return launch_decode_t<DT, D, 3>(p, st);
-    case 4: return launch_decode_t<DT, D, 4>(p, st);
-    case 5: return launch_decode_t<DT, D, 5>(p, st);
-    case 6: return launch_decode_t<DT, D, 6>(p, st);
-    case 7: return launch_decode_t<DT, D, 7>(p, st);
-    case 8: return launch_decode_t<DT, D, 8>(p, st);
+    case 1: return launch_decode_t<DT, D, 1>(p, passes, st);
+    case 2: return launch_decode_t<DT, D, 2>(p, passes, st);
+    case 3: return launch_decode_t<DT, D, 3>(p, passes, st);
+    case 4: return launch_decode_t<DT, D, 4>(p, passes, st);
+    case 5: return launch_decode_t<DT, D, 5>(p, passes, st);
+    case 6: return launch_decode_t<DT, D, 6>(p, passes, st);
+    case 7: return launch_decode_t<DT, D, 7>(p, passes, st);
+    case 8: return launch_decode_t<DT, D, 8>(p, passes, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -580,7 +585,7 @@ int decode_heads_per_wave(int H, int Hkv) {
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, void* o, int B, int H,
                          int Hkv, int max_len, int d, int dt, float scale, int chunk, int n_split, float* ws,
-                         hipStream_t st) {
+                         hipStream_t st, int passes) {
   DecodeParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -599,8 +604,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int3
   p.c = scale * kLog2e;
   const int G = decode_heads_per_wave(H, Hkv);
 #define ATTN_DEC(D_)                                                          \
-  if (dt == DT_F16 && d == D_) return launch_decode_g<DT_F16, D_>(p, G, st); \
-  if (dt == DT_BF16 && d == D_) return launch_decode_g<DT_BF16, D_>(p, G, st);
+  if (dt == DT_F16 && d == D_) return launch_decode_g<DT_F16, D_>(p, G, passes, st); \
+  if (dt == DT_BF16 && d == D_) return launch_decode_g<DT_BF16, D_>(p, G, passes, st);
   ATTN_DEC(64)
   ATTN_DEC(128)
   ATTN_DEC(32)

@@ -167,6 +167,31 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache, con
                     int B, int Hq, int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace,
                     size_t ws_bytes, void* stream);
 
+/* The two passes of attn_decode_gqa as separate calls (page 3, "Kernel design": the
+ * split-K pass writes a partial (m, l, acc) per chunk, a second pass merges them exactly,
+ * without atomics).  attn_decode_split followed by attn_decode_merge on the same stream,
+ * with the same chunk and workspace, gives exactly attn_decode_gqa's output; callers use
+ * the pair to time the passes apart or to run other work between them.
+ *   attn_decode_split: arguments as attn_decode_gqa without `out`; chunk must be given
+ *   (a legal chunk, not 0) and workspace must hold attn_decode_workspace_bytes(B, Hq,
+ *   ceil(max_len / chunk), d) bytes; it is left holding the partials.
+ *   attn_decode_merge: reads those partials (workspace, ws_bytes, B, Hq, max_len, d,
+ *   dtype and chunk as given to the split) and writes out [B][Hq][1][d]. */
+int attn_decode_split(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, int B, int Hq,
+                      int Hkv, int max_len, int d, int dtype, float scale, int chunk, void* workspace, size_t ws_bytes,
+                      void* stream);
+int attn_decode_merge(const void* workspace, size_t ws_bytes, void* out, int B, int Hq, int max_len, int d, int dtype,
+                      int chunk, void* stream);
+
+/* Measurement only, not part of the attention computation: a plain streaming read of
+ * `bytes` (a positive multiple of 16) from DEVICE buffer buf (16-byte aligned) by `waves`
+ * single-wave workgroups, wave w reading the w-th contiguous 1/waves of the buffer with
+ * 16-byte non-temporal loads, as the decode's split waves read their chunks.  It states
+ * the memory-read floor the decode is measured against.  sink: DEVICE buffer of at least
+ * waves * 256 bytes that the kernel may write (in practice it writes nothing).
+ * Asynchronous on `stream`; allocates nothing. */
+int attn_measure_read(const void* buf, size_t bytes, int waves, void* sink, size_t sink_bytes, void* stream);
+
 /* Host-only: the automatic split of attn_decode_gqa (writes HOST *chunk, *n_split).
  * The rule of attn_decode_choose_split over the split waves' columns:
  *   - groups of 3 to 32 query heads (matrix cores): B*Hkv columns, aiming at

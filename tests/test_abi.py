@@ -279,3 +279,26 @@ def test_noalloc_decode_validation():
     assert "scratch" in ea.last_error()
     # One split per head already too large: B*H*(d+2)*4 bytes over the scratch.
     assert call(64, 256, 256, 64, 256, 0) == ea.ATTN_ERR_WORKSPACE
+
+
+def test_decode_pass_and_read_validation():
+    """The separate decode passes and the measurement read refuse bad arguments before
+    any HIP call."""
+    L = ea.lib()
+    split = lambda chunk, ws, wsb: L.attn_decode_split(  # noqa: E731
+        P[0], P[1], P[2], P[4], 2, 3, 3, 100, 64, 0, 0.125, chunk, ws, wsb, None)
+    need = ea.decode_workspace_bytes(2, 3, 4, 64)  # chunk 32 -> 4 splits
+    assert split(0, P[5], need) == ea.ATTN_ERR_INVALID_ARG  # the split pass needs a chunk
+    assert split(32, None, 0) == ea.ATTN_ERR_INVALID_ARG  # and a workspace
+    assert split(32, P[5], need - 1) == ea.ATTN_ERR_WORKSPACE
+    assert split(48, P[5], need) == ea.ATTN_ERR_INVALID_ARG
+    merge = lambda chunk, wsb, out=P[3]: L.attn_decode_merge(P[5], wsb, out, 2, 3, 100, 64, 0, chunk, None)  # noqa: E731
+    assert merge(32, need - 1) == ea.ATTN_ERR_WORKSPACE
+    assert merge(0, need) == ea.ATTN_ERR_INVALID_ARG
+    assert merge(32, need, out=P[5]) == ea.ATTN_ERR_INVALID_ARG  # out aliases the workspace
+    assert merge(32, need, out=None) == ea.ATTN_ERR_INVALID_ARG
+    read = lambda nbytes, waves, sink_bytes: L.attn_measure_read(P[0], nbytes, waves, P[6], sink_bytes, None)  # noqa: E731
+    assert read(100, 1, 256) == ea.ATTN_ERR_INVALID_ARG  # not a multiple of 16
+    assert read(1024, 0, 256) == ea.ATTN_ERR_INVALID_ARG
+    assert read(1024, 65, 65 * 256) == ea.ATTN_ERR_INVALID_ARG  # more waves than 16-byte elements
+    assert read(1024, 4, 4 * 256 - 1) == ea.ATTN_ERR_WORKSPACE

@@ -161,3 +161,34 @@ def test_long_cache_many_splits(heads):
     assert n_split >= 64, (chunk, n_split)
     ref = oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), 1 / np.sqrt(d))
     check(f64(out), ref, "bf16", f"long cache {heads} chunk={chunk} n_split={n_split}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,dtype", [(12, 12, 64, "f16"), (8, 4, 128, "bf16"), (32, 8, 128, "bf16"), (6, 6, 96, "f16")])
+def test_split_then_merge_equals_decode(Hq, Hkv, d, dtype):
+    """attn_decode_split then attn_decode_merge (the two passes as separate calls) give
+    exactly the one-call decode's output with the same chunk and workspace, on the vector
+    (multi-head, pairs of heads) and matrix-core (groups of four) split kernels."""
+    B, max_len = 5, 1500
+    q, kc, vc, lens = W.decode_inputs_gqa(B, Hq, Hkv, max_len, d, dtype, seed=Hq + d, seq_lens=[1500, 1, 733, 64, 1100])
+    qd, kd, vd, ld = (t.to(DEV) for t in (q, kc, vc, lens))
+    for chunk in (64, 224):
+        ns = -(-max_len // chunk)
+        ws = torch.empty(ea.decode_workspace_bytes(B, Hq, ns, d), dtype=torch.uint8, device=DEV)
+        one = ea.decode(qd, kd, vd, ld, scale=0.1, chunk=chunk, workspace=ws).clone()
+        ws2 = torch.empty_like(ws)
+        ea.decode_split(qd, kd, vd, ld, 0.1, chunk, ws2)
+        two = ea.decode_merge(ws2, torch.empty_like(qd), max_len, chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int16), two.view(torch.int16)), chunk
+        check(f64(two), oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), 0.1), dtype, f"two passes chunk={chunk}")
+
+
+def test_measure_read_writes_nothing():
+    """The measurement read streams a buffer and leaves its sink untouched (its loads
+    fold into a checksum that is stored only on a sentinel value the data avoids)."""
+    buf = torch.zeros(3 << 20, dtype=torch.uint8, device=DEV)
+    for waves in (1, 7, 1380, 4096):
+        sink = torch.zeros(waves * 64, dtype=torch.int32, device=DEV)
+        ea.measure_read(buf, waves, sink)
+        torch.cuda.synchronize()
+        assert int(sink.abs().sum()) == 0
