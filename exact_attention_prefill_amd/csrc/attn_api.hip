@@ -195,7 +195,6 @@ int attn_backward(const void* q, const void* k, const void* v, const void* out, 
                   float scale, void* workspace, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_common(B, Hq, N, d, dtype, scale, "N")) != ATTN_OK) return st;
-  if (d == 256) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass has no kernel for d=256");
   if ((st = check_heads(Hq, Hkv)) != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1, got %d", causal);
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||

@@ -54,15 +54,17 @@ constexpr int BN = 64;  // rows of a streamed tile (keys for dQ, query rows for 
 constexpr int NW = 4;   // waves per dK/dV workgroup, 32 keys each
 }  // namespace bwd_cfg
 
-// Chunk keys of a tile row r (16-byte chunks XOR key), by LDS row pitch: rows of 256
-// bytes (d = 96, 128) or of 128 bytes (d = 32, 64; lds_row_bytes pads 32 and 96).
+// Chunk keys of a tile row r (16-byte chunks XOR key), by LDS row pitch: rows of a
+// multiple of 256 bytes (d = 96, 128, 256; the bank pattern repeats every 256 bytes, and
+// keys below 16 keep a chunk within its 256-byte half) or of 128 bytes (d = 32, 64;
+// lds_row_bytes pads 32 and 96).
 template <int D>
 __device__ __forceinline__ int dual_key(int r) {
-  return lds_row_bytes<D>() == 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return lds_row_bytes<D>() % 256 == 0 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int row_key(int r) {
-  return lds_row_bytes<D>() == 256 ? (r & 15) : ((r >> 1) & 7);
+  return lds_row_bytes<D>() % 256 == 0 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Row operand read (A operand of a 32x32x16 MFMA): lane l gets 16 bytes of tile row
@@ -97,10 +99,9 @@ __device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, 
 // LDS-direct loads; physical slot sl of row r receives logical chunk sl ^ key(r).
 // Padded rows (d = 32, 96) have slots past the data, which take a copy of a chunk of
 // the same row and are never read.
-template <int D, bool DUAL, int NW = bwd_cfg::NW>
+template <int D, bool DUAL, int NW = bwd_cfg::NW, int BN = bwd_cfg::BN>
 __device__ __forceinline__ void stage_tile(const uint16_t* src, int row0, int rows_total, char* dst, int wave,
                                            int lane) {
-  constexpr int BN = bwd_cfg::BN;
   constexpr int RBG = 2 * D;                // bytes per row in memory
   constexpr int RB = lds_row_bytes<D>();    // bytes per row in LDS
   constexpr int CH = D / 8;
@@ -158,8 +159,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------------
 // dQ: workgroup = 128 query rows of one (b, h); tiles of 64 keys.
+// d = 256: Q, dO operands and the dQ accumulators alone take 256 registers, so one
+// wave per SIMD.
 template <int DT, int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 8 / NW) void bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = bwd_cfg::BN;
   constexpr int RB = lds_row_bytes<D>(), KS = D / 16, DB = D / 32, BM = 32 * NW;
@@ -565,6 +568,165 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #endif
 }
 
+// ---------------------------------------------------------------------------------
+// dK, dV at d = 256.  The pipelined kernel above would need three sets of 32 KiB Q and
+// dO tiles (192 KiB of LDS) and both full accumulators beside the K and V operands
+// (over 512 registers).  Here a workgroup of four waves owns 128 keys of one (b, kv
+// head), each wave 32 keys whose K and V rows it keeps as MFMA B operands, and streams
+// 32-row Q and dO tiles (double-buffered, 64 KiB) of every query head of the group.
+// The gradients are accumulated in two passes over the halves of d: each pass
+// recomputes S = Q K^T and dP = dO V^T over the full d, forms P and dS as the pipelined
+// kernel does, and adds dV^T += dO^T P and dK^T += Q^T dS for its 128 columns.
+template <int DT, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d256_kernel(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 256, NW = 4, BT = 32;  // waves, rows per streamed tile
+  constexpr int RB = lds_row_bytes<D>(), KS = D / 16, DBH = D / 64;  // d blocks per half
+  constexpr int TILE = BT * RB;
+  constexpr int BK = 32 * NW;
+  __shared__ __attribute__((aligned(1024))) char qbuf[2][TILE];
+  __shared__ __attribute__((aligned(1024))) char dbuf[2][TILE];
+  __shared__ __attribute__((aligned(256))) float lsebuf[2][BT];
+  __shared__ __attribute__((aligned(256))) float dlbuf[2][BT];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
+  const int work = xcd * per + min(xcd, rem) + slot;
+  const int kvbh = __builtin_amdgcn_readfirstlane(work / p.nblk);
+  const int kblk = __builtin_amdgcn_readfirstlane(work - kvbh * p.nblk);
+  const int b = __builtin_amdgcn_readfirstlane(kvbh / p.Hkv);
+  const int kvh = kvbh - b * p.Hkv;
+  const int N = p.N;
+  const int k0 = kblk * BK, kw0 = k0 + 32 * wave, key = kw0 + l32;
+  const bool key_ok = key < N;
+
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = (u32x4){0, 0, 0, 0};
+    vf[ks] = (u32x4){0, 0, 0, 0};
+    if (key_ok) {
+      const size_t off = ((size_t)kvbh * N + key) * D + 16 * ks + 8 * half;
+      kf[ks] = *(const u32x4*)(p.k + off);
+      vf[ks] = *(const u32x4*)(p.v + off);
+    }
+  }
+
+  // Query rows that see any of this block's keys: all of them, or (causal) rows from
+  // the block's first key on, in whole 32-row tiles.
+  const int r_start = CAUSAL ? (k0 / BT) * BT : 0;
+  const int nt = k0 >= N ? 0 : (N - r_start + BT - 1) / BT;
+  const int steps = p.g * nt;  // tiles, over the group's query heads in turn
+
+  if (N % BT != 0) {  // rows past N are never loaded: both sets start from zeros
+    for (int i = tid; i < 2 * TILE / 16; i += 64 * NW) {
+      ((u32x4*)&qbuf[0][0])[i] = (u32x4){0, 0, 0, 0};
+      ((u32x4*)&dbuf[0][0])[i] = (u32x4){0, 0, 0, 0};
+    }
+    for (int i = tid; i < 2 * BT; i += 64 * NW) {
+      (&lsebuf[0][0])[i] = 0.f;
+      (&dlbuf[0][0])[i] = 0.f;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Tile n of the flattened (query head, row tile) order into set n % 2.
+  auto stage = [&](int n) __attribute__((always_inline)) {
+    const int jh = n / nt, j = n - jh * nt, set = n & 1;
+    const int bh = b * p.H + kvh * p.g + jh;
+    const int row0 = r_start + j * BT;
+    stage_tile<D, true, NW, BT>(p.q + (size_t)bh * N * D, row0, N, qbuf[set], wave, lane);
+    stage_tile<D, true, NW, BT>(p.dout + (size_t)bh * N * D, row0, N, dbuf[set], wave, lane);
+    if (wave == 0 && lane < BT) {
+      const int left = N - row0;
+      // Rows past N take lse = +inf, so their P (and dS) is exactly 0 without a test.
+      if (lane >= left) lsebuf[set][lane] = INFINITY;
+      const uint32_t nrec = (uint32_t)(left < BT ? left : BT) * 4;
+      const u32x4 rl = buffer_rsrc(p.lse2 + (size_t)bh * N + row0, nrec);
+      const u32x4 rd = buffer_rsrc(p.delta + (size_t)bh * N + row0, nrec);
+      lds_dma4(rl, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&lsebuf[set][0])));
+      lds_dma4(rd, 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr_of(&dlbuf[set][0])));
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16 dka[DBH], dva[DBH];
+#pragma unroll
+    for (int db = 0; db < DBH; ++db) {
+      dka[db] = (f32x16){};
+      dva[db] = (f32x16){};
+    }
+    if (steps > 0) {
+      stage(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    for (int n = 0; n < steps; ++n) {
+      const int set = n & 1;
+      if (n + 1 < steps) stage(n + 1);  // into the other set, read two tiles ago
+      const char* qb = qbuf[set];
+      const char* dbb = dbuf[set];
+      // S and dP of the tile: entry i of lane l is (row 8(i/4) + 4(l/32) + i%4, key l%32).
+      f32x16 st = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        st = mfma32x32x16<DT>(row_read<D, true>(qb, 0, ks, lane), kf[ks], st);
+        dp = mfma32x32x16<DT>(row_read<D, true>(dbb, 0, ks, lane), vf[ks], dp);
+      }
+      const int row0 = r_start + (n % nt) * BT;
+      const int lo = key - (row0 + 4 * half);  // causal: entries with row offset below lo precede the key
+      u32x4 pf[2], dsf[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *(const f32x4*)(&lsebuf[set][8 * a + 4 * half]);
+        const f32x4 d4 = *(const f32x4*)(&dlbuf[set][8 * a + 4 * half]);
+        float pv[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = __builtin_fmaf(st[4 * a + e], p.c, -l4[e]);
+          if (CAUSAL) x = 8 * a + e >= lo ? x : -INFINITY;
+          pv[e] = fast_exp2(x);
+          dv[e] = pv[e] * (dp[4 * a + e] - d4[e]);
+        }
+        pf[a >> 1][2 * (a & 1)] = pack2<DT>(pv[0], pv[1]);
+        pf[a >> 1][2 * (a & 1) + 1] = pack2<DT>(pv[2], pv[3]);
+        dsf[a >> 1][2 * (a & 1)] = pack2<DT>(dv[0], dv[1]);
+        dsf[a >> 1][2 * (a & 1) + 1] = pack2<DT>(dv[2], dv[3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over this pass's d blocks.
+#pragma unroll
+      for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) {
+          dva[db] = mfma32x32x16<DT>(tr_read<D>(dbb, 0, si, DBH * pass + db, lane), pf[si], dva[db]);
+          dka[db] = mfma32x32x16<DT>(tr_read<D>(qb, 0, si, DBH * pass + db, lane), dsf[si], dka[db]);
+        }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // tile n + 1 is in; set n & 1 is free for tile n + 2
+    }
+    if (key_ok) {
+      const size_t off = ((size_t)kvbh * N + key) * D + 32 * DBH * pass;
+#pragma unroll
+      for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 wk, wv;
+          wk[0] = pack2<DT>(dka[db][4 * a + 0] * p.scale, dka[db][4 * a + 1] * p.scale);
+          wk[1] = pack2<DT>(dka[db][4 * a + 2] * p.scale, dka[db][4 * a + 3] * p.scale);
+          wv[0] = pack2<DT>(dva[db][4 * a + 0], dva[db][4 * a + 1]);
+          wv[1] = pack2<DT>(dva[db][4 * a + 2], dva[db][4 * a + 3]);
+          *(u32x2*)(p.dk + off + 32 * db + 8 * a + 4 * half) = wk;
+          *(u32x2*)(p.dv + off + 32 * db + 8 * a + 4 * half) = wv;
+        }
+    }
+  }
+#endif
+}
+
 // dQ with NWQ waves of 32 query rows per workgroup.
 template <int DT, int D, bool CAUSAL, int NWQ>
 static hipError_t launch_dq(BwdParams p, hipStream_t s) {
@@ -591,13 +753,21 @@ static hipError_t launch_bwd_t(BwdParams p, int num_cus, hipStream_t s) {
   // three per CU), causal grids from four.
   const long long blocks8 = (long long)p.B * p.H * ((p.N + 255) / 256);
   const bool short_wgs = CAUSAL ? p.N <= 4096 : p.N <= 2048;
-  e = blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs ? launch_dq<DT, D, CAUSAL, 8>(p, s)
-                                                                : launch_dq<DT, D, CAUSAL, 4>(p, s);
+  // d = 256 runs one wave per SIMD: four-wave workgroups only.
+  if constexpr (D > 128)
+    e = launch_dq<DT, D, CAUSAL, 4>(p, s);
+  else
+    e = blocks8 >= (CAUSAL ? 4LL : 2LL) * num_cus && !short_wgs ? launch_dq<DT, D, CAUSAL, 8>(p, s)
+                                                                  : launch_dq<DT, D, CAUSAL, 4>(p, s);
   if (e != hipSuccess) return e;
   const int blk = 32 * bwd_cfg::NW;
   p.nblk = (p.N + blk - 1) / blk;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.Hkv)),
-                     dim3(64 * bwd_cfg::NW), 0, s, p);
+  if constexpr (D > 128)
+    hipLaunchKernelGGL((bwd_dkdv_d256_kernel<DT, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.Hkv)),
+                       dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)p.nblk * p.B * p.Hkv)),
+                       dim3(64 * bwd_cfg::NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -635,6 +805,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   ATTN_BW_D(128)
   ATTN_BW_D(32)
   ATTN_BW_D(96)
+  ATTN_BW_D(256)
 #undef ATTN_BW_D
 #undef ATTN_BW
   return hipErrorInvalidValue;

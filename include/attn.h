@@ -235,8 +235,8 @@ int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
  *   workspace : DEVICE buffer of at least attn_backward_workspace_bytes(B, Hq, N) bytes
  *   (16-byte aligned; contents on entry do not matter), or NULL with ws_bytes 0 for a
  *   stream-ordered allocation.
- * Same dtype, layout, validation and asynchrony rules as attn_prefill, except that d
- * is 32, 64, 96 or 128 (ATTN_ERR_UNSUPPORTED for 256).  Deterministic:
+ * Same dtype, layout, validation and asynchrony rules as attn_prefill (d in {32, 64,
+ * 96, 128, 256}).  Deterministic:
  * no atomics, every output element written by one wave. */
 int attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int dtype, int causal,

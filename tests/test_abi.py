@@ -235,7 +235,7 @@ def _backward(**kw):
     "kw,status",
     [
         (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG),
-        (dict(d=256), ea.ATTN_ERR_UNSUPPORTED),  # a forward head size without backward kernels
+        (dict(d=192), ea.ATTN_ERR_UNSUPPORTED),
         (dict(d=80), ea.ATTN_ERR_UNSUPPORTED),
         (dict(lse=None), ea.ATTN_ERR_INVALID_ARG),
         (dict(lse=P[5] + 2), ea.ATTN_ERR_ALIGNMENT),

@@ -41,9 +41,9 @@ def parity(B, Hq, Hkv, N, d, dtype, causal, scale, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 63, 64, 65, 130, 257])
+@pytest.mark.parametrize("N", [1, 31, 33, 63, 64, 65, 130, 257])
 def test_backward_parity(N, causal, d, dtype):
     parity(1, 2, 2, N, d, dtype, causal, 1 / np.sqrt(d), seed=N + d)
 
@@ -56,9 +56,47 @@ def test_backward_grouped_heads(heads, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_backward_many_tiles(d, causal):
     parity(1, 4, 2, 700, d, "f16" if d in (32, 64) else "bf16", causal, 1 / np.sqrt(d), seed=7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d256(causal):
+    """Head size 256 (one wave per SIMD; dK and dV summed in two passes over the halves
+    of d): grouped heads (groups of 3 and of 1), a negative scale, several key blocks
+    and a ragged last tile, both dtypes."""
+    parity(2, 6, 2, 300, 256, "bf16", causal, 0.0625, seed=256)
+    parity(1, 3, 3, 161, 256, "f16", causal, -0.05, seed=257)
+    parity(1, 4, 1, 129, 256, "bf16", causal, 0.0625, seed=258)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d256_sampled_long(causal):
+    """d = 256 at 8 heads of 4100 tokens (many key blocks and Q/dO tiles, ragged last
+    tile): sampled dq rows and dk/dv key rows against the row-sampled oracle."""
+    from parity import backward_bounds_keys, backward_bounds_rows
+
+    B, H, N, d = 1, 8, 4100, 256
+    scale = 1 / np.sqrt(d)
+    q, k, v = W.prefill_inputs(B, H, N, d, "bf16", seed=41)
+    dout = W.prefill_inputs(B, H, N, d, "bf16", seed=42)[0]
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ea.prefill(qd, kd, vd, causal=causal, scale=scale, lse=True)
+    dq, dk, dv = ea.backward(qd, kd, vd, out, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = sorted(set(W.prefill_rows_sample(N, 10, seed=43)) | {1, 2, 31, 32, 33, 4096, 4099})
+    for h in (0, H - 1):
+        qf, kf, vf, df = (f64(t[:, h:h + 1]) for t in (q, k, v, dout))
+        ref = oracle.backward_dq_rows(qf, kf, vf, df, causal, scale, 0, 0, rows)
+        bq = backward_bounds_rows(qf, kf, vf, df, causal, scale, 0, 0, rows)
+        check_grad(f64(dq[0, h, rows]), ref, bq, "bf16", f"d256 dq h={h} causal={causal}")
+        rk, rv = oracle.backward_dkdv_rows(qf, kf, vf, df, causal, scale, 0, 0, rows)
+        bk, bv = backward_bounds_keys(qf, kf, vf, df, causal, scale, 0, 0, rows)
+        check_grad(f64(dk[0, h, rows]), rk, bk, "bf16", f"d256 dk h={h} causal={causal}")
+        check_grad(f64(dv[0, h, rows]), rv, bv, "bf16", f"d256 dv h={h} causal={causal}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
