@@ -72,7 +72,7 @@ DERIVED_SLOTS = {"FETCH_SIZE": {"TCC": 3}, "WRITE_SIZE": {"TCC": 2}}
 
 # Kernels of the headline workloads, by template signature.
 KERNELS = {
-    "prefill": "attn::prefill_kernel<1, 128, false, 8, 1, false>",
+    "prefill": "attn::prefill_kernel<1, 128, false, 8, 1, 2, 1>",
     "decode_split": "attn::decode_split_kernel<0, 64, 1>",
     "decode_merge": "attn::decode_merge_kernel<0, 64, 4>",
     "gqa_split": "attn::decode_split_mfma_kernel<1, 128>",
@@ -80,6 +80,7 @@ KERNELS = {
     "bwd_delta": "attn::bwd_delta_kernel<1, 128>",
     "bwd_dq": "attn::bwd_dq_kernel<1, 128, false, 8>",
     "bwd_dkdv": "attn::bwd_dkdv_kernel<1, 128, false>",
+    "read_floor": "attn::measure_read_kernel",
 }
 # Prefill sources whose hash keys the stored traffic figure (the same files bench.py hashes).
 PREFILL_SOURCES = ["exact_attention_prefill_amd/csrc/prefill.hip", "exact_attention_prefill_amd/csrc/attn_device.h"]
@@ -237,19 +238,21 @@ def summarize(out: str):
     def kernel_slices(key, dispatches, kind):
         """The dispatches of one kernel that the figures describe.  The bench runs, in
         order: untimed clock-settling steps (as many as fit in its settle time), W
-        warm-up steps and K timed steps (a prefill and a decode each), then the cold
-        decode calls, then the prefill launches that also write the log-sum-exp.  The
-        settling steps are counted from the decode's dispatches; the prefill figures
-        take the K timed launches and the decode figures the cold calls."""
+        warm-up steps and K timed steps (a prefill and a decode each), then I cold
+        decode calls, then I cold calls of the two passes apart (attn_decode_split and
+        attn_decode_merge: the same kernels), then the prefill launches that also write
+        the log-sum-exp.  The settling steps are counted from the decode's dispatches;
+        the prefill figures take the K timed launches and the decode figures the I cold
+        one-call decodes."""
         sig = KERNELS[key]
         W_, K_, I_ = run_shape[kind]
-        settle = len(select(dispatches, KERNELS["decode_split"])) - (W_ + K_) - I_
+        settle = len(select(dispatches, KERNELS["decode_split"])) - (W_ + K_) - 2 * I_
         if settle < 0:
             settle = 0
         if key == "prefill":
             return select(dispatches, sig, settle + W_, K_)
         if key in ("decode_split", "decode_merge"):
-            return select(dispatches, sig, settle + W_ + K_)
+            return select(dispatches, sig, settle + W_ + K_, I_)
         return select(dispatches, sig)
 
     fc = calibration(pmc.get("fetch", []), "FETCH_SIZE", CALIBRATE_MIB * 1024)
@@ -306,6 +309,9 @@ def summarize(out: str):
         "decode_us_split_plus_merge": dec_us, "decode_gbs": dec_gbs,
         "decode_frac": dec_gbs / PEAK_HBM_GBS if dec_gbs else None, "decode_algorithmic_bytes": dec_bytes,
         "decode_split_hbm_bytes": ds.get("hbm_bytes"),
+        "read_floor_us": rows["read_floor"].get("avg_us"),
+        "read_floor_gbs": dec_bytes / (rows["read_floor"]["avg_us"] * 1e-6) / 1e9
+        if dec_bytes and rows["read_floor"].get("avg_us") else None,
     }
     with open(os.path.join(out, "summary.json"), "w") as f:
         json.dump({"agent": {"cus": cus, "simd_per_cu": simd_per_cu, "xcds": n_xcd, "peak_mhz": peak_mhz},

@@ -88,6 +88,8 @@ def run_dir(tmp_path):
     for _ in range(ev.TRACE_STEPS):  # the timed steps: prefill then decode (warm)
         seq += [(PRE, 2_000_000), (SPLIT, 999_999), (MERGE, 999_999)]
     seq += [(SPLIT, 15_000), (MERGE, 5_000)] * ev.TRACE_DECODE_ITERS  # cold decode
+    seq += [(SPLIT, 17_000), (MERGE, 7_000)] * ev.TRACE_DECODE_ITERS  # the passes apart: not the figure
+    seq += [(ev.KERNELS["read_floor"], 12_800)] * ev.TRACE_DECODE_ITERS  # the plain read
     seq += [(PRE, 9_000_000)] * 3  # later launches with the lse output: not the step's
     _trace(os.path.join(out, "trace", "h", "run_kernel_trace.csv"), seq)
     flop = 4.0 * 16 * 16384 * 16384 * 128
@@ -105,6 +107,7 @@ def run_dir(tmp_path):
         for _ in range(n_pmc):
             s += [(PRE, 1_000_000, {counter: pre_val}), (SPLIT, 1, {counter: 1e9}), (MERGE, 1, {counter: 1e9})]
         s += [(SPLIT, 1, {counter: split_val}), (MERGE, 1, {counter: 0.0})] * ev.PMC_DECODE_ITERS
+        s += [(SPLIT, 1, {counter: 3e9}), (MERGE, 1, {counter: 3e9})] * ev.PMC_DECODE_ITERS  # passes apart
         s += [(PRE, 1_000_000, {counter: 1e12})]  # an lse launch: excluded
         s += [("__amd_rocclr_copyBuffer", 100, {counter: copy_val})] * 3
         return s
@@ -117,7 +120,7 @@ def run_dir(tmp_path):
     mf = [(PRE, 1_000_000, {"GRBM_GUI_ACTIVE": 3.0e6, "SQ_VALU_MFMA_BUSY_CYCLES": 6.0e6, "SQ_INSTS_MFMA": 1.875e5,
                             "SQ_VALU_MFMA_COEXEC_CYCLES": 1.2e6}),
           (SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * n_pmc
-    mf += [(SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * ev.PMC_DECODE_ITERS
+    mf += [(SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * (2 * ev.PMC_DECODE_ITERS)
     _pmc(os.path.join(out, "mfma", "h", "run_counter_collection.csv"), mf)
     return out
 
@@ -131,6 +134,8 @@ def test_summary_derivations(run_dir):
     assert d["prefill_trace_vs_events"] == pytest.approx(2.0 / 2.02)
     assert d["decode_us_split_plus_merge"] == pytest.approx(20.0)  # cold calls only
     assert d["decode_gbs"] == pytest.approx(64e6 / 20e-6 / 1e9)
+    assert d["read_floor_us"] == pytest.approx(12.8)
+    assert d["read_floor_gbs"] == pytest.approx(64e6 / 12.8e-6 / 1e9)
     # FETCH factor 2 (copy read half), WRITE factor 1
     assert d["prefill_hbm_bytes"] == pytest.approx((1000.0 * 2 + 300.0) * 1024)
     assert d["decode_split_hbm_bytes"] == pytest.approx((500.0 * 2 + 2.0) * 1024)
@@ -153,3 +158,15 @@ def test_stored_traffic_key_matches_what_bench_hashes():
 
     assert [os.path.relpath(p, ev.ROOT) for p in bench.KERNEL_SOURCES] == ev.PREFILL_SOURCES
     assert bench.kernel_hash() == ev.source_hash(ev.PREFILL_SOURCES)
+
+
+def test_committed_counters_match_the_prefill_sources():
+    """profiles/prefill_headline_counters.json must have been taken on the prefill sources
+    in the tree (bench.py reports its traffic only then): re-take it after any change."""
+    import bench
+
+    with open(bench.COUNTERS) as f:
+        c = json.load(f)
+    assert c["kernel_sha"] == bench.kernel_hash(), "re-run the evidence harness: the prefill sources changed"
+    assert c["kernel"] == "void " + ev.KERNELS["prefill"] + "(attn::PrefillParams)"
+    assert bench.measured_traffic() == c["hbm_bytes_per_launch"]
