@@ -330,7 +330,8 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   };
   // P dword w (of 8) of a unit, in three steps that the schedule spreads over
   // consecutive issue slots: x = c s - m (two FMAs), e = 2^x, then round to 16 bits,
-  // pack and add into the unit's row sum.
+  // pack and add into the unit's row sum.  The sum runs as two chains (even and odd
+  // dwords), added at the end of the unit: half the dependent latency before the guard.
   auto p_arg = [&](const f32x16& sc, float nm, int w, float (&x)[2]) __attribute__((always_inline)) {
     x[0] = __builtin_fmaf(sc[2 * w], p.c, nm);
     x[1] = __builtin_fmaf(sc[2 * w + 1], p.c, nm);
@@ -339,21 +340,22 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
     x[0] = fast_exp2(x[0]);
     x[1] = fast_exp2(x[1]);
   };
-  auto p_pack = [&](const float (&e)[2], u32x4 (&pf)[2], float& l_unit, int w) __attribute__((always_inline)) {
+  auto p_pack = [&](const float (&e)[2], u32x4 (&pf)[2], float (&l2)[2], int w) __attribute__((always_inline)) {
     const uint32_t t = pack2<DT>(e[0], e[1]);
     pf[w >> 2][w & 3] = t;
-    l_unit = add_pair<DT>(t, l_unit);
+    l2[w & 1] = add_pair<DT>(t, l2[w & 1]);
   };
   // All of a unit's P with the given -m (the slow path and the prologue).
   auto p_all = [&](const f32x16& sc, u32x4 (&pf)[2], float& l_unit, float nm) __attribute__((always_inline)) {
-    l_unit = 0.f;
+    float l2[2] = {0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float x[2];
       p_arg(sc, nm, w, x);
       p_exp(x);
-      p_pack(x, pf, l_unit, w);
+      p_pack(x, pf, l2, w);
     }
+    l_unit = l2[0] + l2[1];
   };
 
   // One pipeline iteration u of this wave, a three-stage pipeline over units:
@@ -394,11 +396,13 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
                      u32x4 (&vf)[R]) __attribute__((always_inline)) {
     const int kg = h * KS, vg = h * NP;  // ring positions of this unit's operand 0
     float l_unit[QB];
+    float l2[QB][2];
     float xa[QB][2], xb[QB][2];  // P arguments / exponentials in flight, two dwords apart
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) {
       mask_unit(scur[cb], u + 1, cb);  // a unit past this wave's keys masks entirely: p = 0
-      l_unit[cb] = 0.f;
+      l2[cb][0] = 0.f;
+      l2[cb][1] = 0.f;
     }
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) p_arg(scur[cb], neg_m[cb], 0, xa[cb]);
@@ -428,18 +432,19 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
         float (&cur_x)[2] = (i & 1) ? xb[cb] : xa[cb];
         float (&oth_x)[2] = (i & 1) ? xa[cb] : xb[cb];
         p_exp(cur_x);
-        if (i >= 1) p_pack(oth_x, pnext[cb], l_unit[cb], i - 1);
+        if (i >= 1) p_pack(oth_x, pnext[cb], l2[cb], i - 1);
         if (i + 1 < 8) p_arg(scur[cb], neg_m[cb], i + 1, oth_x);
         // Anchor this slot's VALU results in the slot: IR-level code motion ignores
         // sched_barrier and would otherwise gather the softmax after the MFMAs.
-        asm volatile("" ::"v"(cur_x[0]), "v"(cur_x[1]), "v"(oth_x[0]), "v"(oth_x[1]), "v"(l_unit[cb]));
+        asm volatile("" ::"v"(cur_x[0]), "v"(cur_x[1]), "v"(oth_x[0]), "v"(oth_x[1]), "v"(l2[cb][0]), "v"(l2[cb][1]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     bool over = false;
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) {
-      p_pack((7 & 1) ? xb[cb] : xa[cb], pnext[cb], l_unit[cb], 7);
+      p_pack((7 & 1) ? xb[cb] : xa[cb], pnext[cb], l2[cb], 7);
+      l_unit[cb] = l2[cb][0] + l2[cb][1];
       over = over || (l_unit[cb] > kSumGuard);
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {  // rare: laid out off the hot path

@@ -2,6 +2,7 @@
 
     python -m exact_attention_prefill_amd.evidence --out DIR [--passes trace,fetch,write,mfma,lds,wave]
     python -m exact_attention_prefill_amd.evidence --out DIR --summarize-only
+    python -m exact_attention_prefill_amd.evidence --out DIR --workloads [--summarize-only]
 
 Runs ``bench.py`` under rocprofv3 once per pass -- a kernel trace, then one counter set
 per run, because rocprofv3 collects a set in a single pass and refuses sets that exceed
@@ -22,6 +23,10 @@ What it derives, per attention kernel:
   from GRBM_GUI_ACTIVE per XCD and the clock from those cycles over the dispatch
   time, cross-checked by the instruction count (SQ_INSTS_MFMA x 32 cycles for the
   32x32x16 MFMA every one of these kernels uses).
+
+``--workloads`` instead traces the default bench once (every prefill workload it times)
+and writes ``DIR/prefill_workloads_kernel_trace.md``: per workload, its launch form, its
+grid and the median dispatch time of its timed calls.
 
 The parent process never touches the GPU: every pass is a child process, and the
 program follows rocprofv3's ``--`` directly (the Python interpreter, no launcher).
@@ -339,7 +344,7 @@ def _fmt(x, spec):
 def render(out, rows, derived, agent, fc, wc, sha):
     cus, spc, nx, mhz = agent
     rel = os.path.relpath(out, ROOT)
-    lines = ["# rocprofv3 evidence: headline prefill, ragged decode, grouped decode, backward", "",
+    lines = ["# rocprofv3 evidence: headline prefill, ragged decode, grouped decode, backward, read floor", "",
              f"Made by `python -m exact_attention_prefill_amd.evidence --out {rel}`, which ran, from the",
              f"repository root with TMPDIR=/tmp, one command per pass (`<out>` = `{rel}`):", "", "```"]
     for name in ALL_PASSES:
@@ -381,8 +386,135 @@ def render(out, rows, derived, agent, fc, wc, sha):
               f"- decode: split + merge {_fmt(d['decode_us_split_plus_merge'], '.2f')} us (kernel time) = "
               f"{_fmt(d['decode_gbs'], '.0f')} GB/s = {_fmt(d['decode_frac'], '.1%')} of {PEAK_HBM_GBS:.0f} GB/s for "
               f"{_fmt(d['decode_algorithmic_bytes'], 'd')} algorithmic bytes; split HBM "
-              f"{_fmt(d['decode_split_hbm_bytes'] / 1e6 if d['decode_split_hbm_bytes'] else None, '.2f')} MB", ""]
+              f"{_fmt(d['decode_split_hbm_bytes'] / 1e6 if d['decode_split_hbm_bytes'] else None, '.2f')} MB",
+              f"- read floor: {_fmt(d['read_floor_us'], '.2f')} us = {_fmt(d['read_floor_gbs'], '.0f')} GB/s for the same "
+              f"bytes", "",
+              "## Notes", "",
+              f"- `{KERNELS['read_floor']}` is the decode's read floor: a plain cold read of the ragged decode's bytes",
+              "  by as many waves as the split pass has non-empty chunks, each reading one contiguous span with",
+              "  non-temporal 16-byte loads (`attn_measure_read`, measurement only), against which the split pass",
+              "  and the merge's dependent launch are measured.",
+              f"- The clock under the headline prefill was {_fmt(d['prefill_clock_ghz'], '.2f')} GHz on this box. The",
+              "  MI355X clock under this load is power-limited and differs from box to box (1.83-1.98 GHz over the",
+              "  recorded runs of the same binary), and the prefill's time follows it.", ""]
     return "\n".join(lines)
+
+
+WORKLOADS_DIR = "cfgtrace"
+
+
+def workloads_command(out: str, python: str = sys.executable):
+    """A kernel trace of the default bench (every prefill workload it times)."""
+    return ["timeout", "-k", "10", "600", "rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv",
+            "-d", os.path.join(out, WORKLOADS_DIR), "-o", "run", "--", python, "-u", "bench.py", "--steps", "3",
+            "--warmup", "1", "--no-cpu-baseline"]
+
+
+def _form_of(case, cus: int):
+    """(kernel signature, grid threads) of a workload's prefill launch, and its workgroups."""
+    import exact_attention_prefill_amd as ea
+
+    p = ea.prefill_plan(case.B, case.H, case.N, case.d, case.causal, cus)
+    rows = p["rows_per_wave"] * p["waves"] // p["key_groups"]
+    wgs = -(-case.N // rows) * case.H * case.B
+    sig = (f"void attn::prefill_kernel<{1 if case.dtype == 'bf16' else 0}, {case.d}, "
+           f"{'true' if case.causal else 'false'}, {p['waves']}, {p['rows_per_wave'] // 32}, {p['stages']}, "
+           f"{p['key_groups']}>(attn::PrefillParams)")
+    return (sig, wgs * 64 * p["waves"]), wgs
+
+
+def summarize_workloads(out: str, cus: int = 256):
+    """Each prefill workload's dispatches in a kernel trace of the default bench.
+
+    The bench runs the head-size sweep after the step and the backward pass, then the
+    workloads in its own order, so each workload's dispatches form one contiguous run of
+    its (kernel, grid) there; the three d = 128 token splits share one form and grid and
+    run back to back, told apart by duration.  The median is over a run's last 110
+    dispatches (the timed calls and, for launch-sized calls, their graph replays)."""
+    import math
+
+    sys.path.insert(0, ROOT)
+    import workloads as W
+
+    trace = os.path.join(out, WORKLOADS_DIR, "run_kernel_trace.csv")
+    with open(trace) as f:
+        rows = [r for r in csv.DictReader(f) if r.get("Kind", "KERNEL_DISPATCH") == "KERNEL_DISPATCH"]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rec = None
+    log_path = os.path.join(out, WORKLOADS_DIR + ".log")
+    if os.path.exists(log_path):
+        with open(log_path) as f:
+            for line in f:
+                if line.startswith("{"):
+                    rec = json.loads(line)
+    runs = []
+    for r in rows:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]))
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(dur)
+        else:
+            runs.append([key, [dur]])
+    sweep = [W.PrefillCase(f"head size d={d}: B=1 H=16 N=16384 bf16 full", 1, 16, 16384, d, "bf16", False,
+                           1 / math.sqrt(d)) for d in (32, 64, 96, 128, 256)]
+    order = sweep + list(W.SMALL_F16 + W.GPT2_F16 + W.GPT2_SWEEP + W.DENSE_D128 + W.LONG)
+    pos = max(i for i, r in enumerate(runs) if "bwd_dkdv" in r[0][0]) + 1
+    bands = {4096: (0, 700e3), 8192: (700e3, 1.4e6), 16384: (1.4e6, 1e12)}
+    table = []
+    for c in order:
+        key, wgs = _form_of(c, cus)
+        dense = c in W.DENSE_D128
+        if dense and c.N != 4096:
+            j = pos - 1
+        else:
+            j = next((i for i in range(pos, len(runs)) if runs[i][0] == key), None)
+        durs = runs[j][1] if j is not None else []
+        if dense:
+            lo, hi = bands[c.N]
+            durs = [x for x in durs if lo <= x < hi]
+        if j is not None:
+            pos = j + 1
+        med = statistics.median(durs[-min(len(durs), 110):]) / 1e3 if durs else None
+        ev = None
+        if rec:
+            cfg = rec.get("configs", {}).get(c.name)
+            if cfg:
+                ev = cfg.get("graph_ms", cfg["ms"]) * 1e3
+            elif c.name.startswith("head size"):
+                ev = rec["head_sizes"]["by_d"][str(c.d)]["ms"] * 1e3
+        tf = c.flop / (med * 1e-6) / 1e12 if med else None
+        form = key[0].replace("void attn::prefill_kernel", "").replace("(attn::PrefillParams)", "")
+        table.append((c.name, form, wgs, len(durs), med, tf, ev))
+    rel = os.path.relpath(out, ROOT)
+    cmd = " ".join(workloads_command("<out>", python="python3"))
+    head_tf = rec.get("value") if rec else None
+    lines = ["# Kernel trace: every prefill workload of the default bench", "",
+             f"Made by `python -m exact_attention_prefill_amd.evidence --out {rel} --workloads`, which ran, from",
+             f"the repository root with TMPDIR=/tmp (`<out>` = `{rel}`):", "", "```", cmd, "```", "",
+             f"Prefill sources (prefill.hip + attn_device.h) sha256[:16] `{source_hash(PREFILL_SOURCES)}`. Each",
+             "workload's row holds the `attn::prefill_kernel` dispatches of its launch form and grid, taken in the",
+             "order the bench runs the workloads (each one's dispatches form one contiguous run in the trace; the",
+             "three d = 128 token splits share one form and grid and run back to back, told apart by duration:",
+             "below 0.7 ms, 0.7-1.4 ms, above). The form (template arguments) and the grid follow from",
+             f"`attn_prefill_plan` for {cus} CUs. The median is over the run's last 110 dispatches (the timed calls",
+             "and, for launch-sized calls, their graph replays); flop is 4·B·H·N²·d, halved when causal. The last",
+             "column is bench.py's own timing from the same run: HIP events around one call, or per call of a",
+             "replayed HIP graph of 20 calls for the launch-sized workloads (their trace medians exclude the",
+             "host's launch overhead too).",
+             f"The headline step ran at {_fmt(head_tf, '.1f')} TFLOP/s under the tracer on this box.", "",
+             "| workload | form `<dt, d, causal, waves, blocks/wave, stages, key groups>` | workgroups | "
+             "dispatches in its run | trace median us (last 110) | TFLOP/s | bench us (events; graph replays where "
+             "launch-sized) |",
+             "|---|---|---|---|---|---|---|"]
+    for name, form, wgs, n, med, tf, ev in table:
+        lines.append(f"| {name} | `{form}` | {wgs} | {n} | {_fmt(med, '.2f')} | {_fmt(tf, '.1f')} | {_fmt(ev, '.2f')} |")
+    speedup = rec.get("configs", {}).get("causal_speedup") if rec else None
+    if speedup:
+        lines += ["", f"Causal speed-up (full time over causal time, bench.py, same run): {json.dumps(speedup)}."]
+    path = os.path.join(out, "prefill_workloads_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 def main(argv=None):
@@ -390,9 +522,23 @@ def main(argv=None):
     ap.add_argument("--out", required=True, help="output folder for the rocprofv3 files and the summary")
     ap.add_argument("--passes", default=",".join(ALL_PASSES))
     ap.add_argument("--summarize-only", action="store_true")
+    ap.add_argument("--workloads", action="store_true", help="trace every prefill workload of the default bench")
     a = ap.parse_args(argv)
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
+    if a.workloads:
+        ok = True
+        if not a.summarize_only:
+            cmd = workloads_command(out)
+            print(f"[evidence] workloads: {' '.join(cmd)}", flush=True)
+            with open(os.path.join(out, WORKLOADS_DIR + ".log"), "w") as log:
+                r = subprocess.run(cmd, cwd=ROOT, env=dict(os.environ, TMPDIR="/tmp"), stdout=log,
+                                   stderr=subprocess.STDOUT)
+            print(f"[evidence] workloads exit {r.returncode}", flush=True)
+            ok = r.returncode == 0
+        if ok:
+            print(summarize_workloads(out), flush=True)
+        return 0 if ok else 1
     passes = [p for p in a.passes.split(",") if p]
     for p in passes:
         if p not in ALL_PASSES:

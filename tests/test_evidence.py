@@ -170,3 +170,49 @@ def test_committed_counters_match_the_prefill_sources():
     assert c["kernel_sha"] == bench.kernel_hash(), "re-run the evidence harness: the prefill sources changed"
     assert c["kernel"] == "void " + ev.KERNELS["prefill"] + "(attn::PrefillParams)"
     assert bench.measured_traffic() == c["hbm_bytes_per_launch"]
+
+
+def test_workloads_summary_matches_a_synthetic_trace(tmp_path):
+    """A trace laid out in the bench's order (the backward pass, then the head-size sweep
+    and the workloads, each a run of its own launch form and grid; the three d = 128
+    token splits one run told apart by duration): every workload's row gets its own
+    dispatches, form and grid, and the bench's timing from the log line."""
+    import math
+
+    import workloads as W
+
+    out = str(tmp_path)
+    sweep = [W.PrefillCase(f"head size d={d}: B=1 H=16 N=16384 bf16 full", 1, 16, 16384, d, "bf16", False,
+                           1 / math.sqrt(d)) for d in (32, 64, 96, 128, 256)]
+    order = sweep + list(W.SMALL_F16 + W.GPT2_F16 + W.GPT2_SWEEP + W.DENSE_D128 + W.LONG)
+    band = {4096: 500_000, 8192: 1_000_000, 16384: 1_800_000}
+    rows, t, want = [["KERNEL_DISPATCH", "void attn::bwd_dkdv_kernel<1, 128, false>(attn::BwdParams)", 1, 0, 0]], 10, {}
+    configs, by_d = {}, {}
+    for i, c in enumerate(order):
+        (sig, grid), wgs = ev._form_of(c, 256)
+        dur = band[c.N] if c in W.DENSE_D128 else 20_000 + 1_000 * i
+        for _ in range(3):
+            rows.append(["KERNEL_DISPATCH", sig, grid, t, t + dur])
+            t += dur + 10
+        want[c.name] = (sig, wgs, dur / 1e3)
+        if c.name.startswith("head size"):
+            by_d[str(c.d)] = {"ms": dur / 1e6 * 1.01}
+        else:
+            configs[c.name] = {"ms": dur / 1e6 * 1.02}
+    _write(os.path.join(out, ev.WORKLOADS_DIR, "run_kernel_trace.csv"),
+           ["Kind", "Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"], rows)
+    with open(os.path.join(out, ev.WORKLOADS_DIR + ".log"), "w") as f:
+        f.write("[bench] a log line\n")
+        f.write(json.dumps({"value": 1234.5, "configs": configs, "head_sizes": {"by_d": by_d}}) + "\n")
+    md = open(ev.summarize_workloads(out)).read()
+    assert "1234.5 TFLOP/s" in md and ev.source_hash(ev.PREFILL_SOURCES) in md
+    table = {ln.split(" | ")[0][2:]: ln.split(" | ") for ln in md.splitlines()
+             if ln.startswith("| ") and "`<" in ln and not ln.startswith("| workload |")}
+    assert set(table) == set(want)
+    for name, (sig, wgs, us) in want.items():
+        cells = table[name]
+        form = sig.replace("void attn::prefill_kernel", "").replace("(attn::PrefillParams)", "")
+        assert cells[1] == f"`{form}`" and int(cells[2]) == wgs and int(cells[3]) == 3, name
+        assert float(cells[4]) == pytest.approx(us, abs=0.01), name
+        factor = 1.01 if name.startswith("head size") else 1.02
+        assert float(cells[6].rstrip(" |")) == pytest.approx(us * factor, abs=0.01), name
