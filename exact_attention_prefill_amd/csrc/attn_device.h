@@ -22,6 +22,16 @@ enum { DT_F16 = 0, DT_BF16 = 1 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Work-item and workgroup indices from the compiler's builtins.  HIP's threadIdx and
+// blockIdx read them through device-library functions that are compiled with the
+// default IEEE mode; this library is compiled with it off (-mno-amdgpu-ieee), and the
+// inliner does not inline across that difference, which would leave real calls (and a
+// stack) at every kernel's entry.  Grid sizes come from each kernel's parameters.
+__device__ __forceinline__ int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int group_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int group_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int group_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+
 // acc += A * B for a 32x32 output block and a 16-deep contraction.  Each lane holds
 // eight 16-bit elements of A and of B; the lane -> (row, k) assignment is the
 // hardware's, and only needs to be the same for A and B.

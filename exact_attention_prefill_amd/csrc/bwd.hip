@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   constexpr int LPR = CH == 12 ? 16 : CH;    // lanes per row (a power of two)
   constexpr int RPB = 256 / LPR;
   const long long total = (long long)p.B * p.H * p.N;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int seg = threadIdx.x % LPR;
+  const long long row = (long long)group_x() * RPB + thread_x() / LPR;
+  const int seg = thread_x() % LPR;
   float acc = 0.f;
   if (row < total && seg < CH) {
     const u32x4 a = *(const u32x4*)(p.o + row * D + seg * 8);
@@ -172,10 +172,10 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 8 / NW) void bwd_dq_kernel(B
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int G = gridDim.x, bid = blockIdx.x;
+  const int G = p.nblk * p.B * p.H, bid = group_x();  // the grid: query blocks x heads x batch
   const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
   const int work = xcd * per + min(xcd, rem) + slot;
   const int bh = __builtin_amdgcn_readfirstlane(work / p.nblk);
@@ -242,11 +242,16 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 8 / NW) void bwd_dq_kernel(B
     f32x16 ds;
     // Entry i holds key 32u + 4half + 8(i/4) + i%4: visible iff its offset 8(i/4) + i%4
     // (a constant) is below lim.
-    const int lim = key_end - 32 * u - 4 * half;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pr = fast_exp2(__builtin_fmaf(st[i], p.c, -lse2));
-      ds[i] = 8 * (i >> 2) + (i & 3) < lim ? pr * (dpt[i] - dl) : 0.f;
+    for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(__builtin_fmaf(st[i], p.c, -lse2)) * (dpt[i] - dl);
+    // Only the sequence's last unit and (causal) the wave's diagonal unit hold entries a
+    // row cannot see: there, those entries are replaced by 0 (a select, so whatever the
+    // arithmetic gave them is dropped); every other unit skips the per-entry test.
+    const bool need = (32 * u + 32 > N) || (CAUSAL && 32 * u + 31 > qw0);
+    if (__builtin_expect(need, 0)) {
+      const int lim = key_end - 32 * u - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = 8 * (i >> 2) + (i & 3) < lim ? ds[i] : 0.f;
     }
     u32x4 dsf[2];
     pack_unit<DT>(ds, dsf);
@@ -314,10 +319,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lsebuf[NS][BN];
   __shared__ __attribute__((aligned(256))) float dlbuf[NS][BN];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int G = gridDim.x, bid = blockIdx.x;
+  const int G = p.nblk * p.B * p.Hkv, bid = group_x();  // the grid: key blocks x K/V heads x batch
   const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
   const int work = xcd * per + min(xcd, rem) + slot;
   const int kvbh = __builtin_amdgcn_readfirstlane(work / p.nblk);
@@ -589,10 +594,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d256_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lsebuf[2][BT];
   __shared__ __attribute__((aligned(256))) float dlbuf[2][BT];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int G = gridDim.x, bid = blockIdx.x;
+  const int G = p.nblk * p.B * p.Hkv, bid = group_x();  // the grid: key blocks x K/V heads x batch
   const int xcd = bid & 7, slot = bid >> 3, per = G >> 3, rem = G & 7;
   const int work = xcd * per + min(xcd, rem) + slot;
   const int kvbh = __builtin_amdgcn_readfirstlane(work / p.nblk);

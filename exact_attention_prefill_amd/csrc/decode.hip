@@ -49,13 +49,13 @@ struct DecodeParams {
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
 
-// Split handled by this workgroup of a (n_split, columns...) grid.  Workgroups are
+// Split handled by this workgroup of an (n_split, ny, B) grid.  Workgroups are
 // dealt to the 8 XCDs round-robin by linear id, so with a split count that is a
 // multiple of 8 split s of every column would land on XCD s mod 8; the sequences'
 // non-empty splits are prefixes, which would load the low XCDs more.  Skewing the
 // split by the column index starts each column on another XCD.
-__device__ __forceinline__ int skewed_split(int n_split) {
-  return (int)((blockIdx.x + blockIdx.y + (unsigned)blockIdx.z * gridDim.y) % (unsigned)n_split);
+__device__ __forceinline__ int skewed_split(int n_split, int ny) {
+  return (int)(((unsigned)group_x() + group_y() + (unsigned)group_z() * ny) % (unsigned)n_split);
 }
 
 // Dot product of two packed pairs of 16-bit values, accumulated in fp32.
@@ -97,13 +97,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 :
   constexpr int RPW = 64 / LPR;              // rows per wave-wide load
   constexpr int RITER = RPW * kUnroll;
 
-  const int b = blockIdx.z;
-  const int s = skewed_split(p.n_split);
-  const int h0 = blockIdx.y * G;  // first query head of this wave
+  const int b = group_z();
+  const int s = skewed_split(p.n_split, p.H / G);
+  const int h0 = group_y() * G;  // first query head of this wave
   const int kvh = h0 / p.g;       // the K/V head all G of them read
   const int L = clamp_len(p.seq_lens[b], p.max_len);
   const int r0 = s * p.chunk;
-  const int lane = threadIdx.x;
+  const int lane = thread_x();
   const size_t pair0 = (size_t)b * p.H + h0;  // (b, h0) as a query-head pair index
   if (r0 >= L) {  // empty chunk: mark it so the merge needs no lengths
     if (lane < G) *(float2*)(p.ws_ml + ((pair0 + lane) * p.n_split + s) * 2) = make_float2(-INFINITY, 0.f);
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
 
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int s = skewed_split(p.n_split);
-  const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+  const int kvh = group_y(), b = group_z();
+  const int s = skewed_split(p.n_split, p.Hkv);
+  const int lane = thread_x(), l32 = lane & 31, half = lane >> 5;
   const int g = p.g;
   // Uniform values the buffer descriptors are built from are pinned to SGPRs.
   const int L = __builtin_amdgcn_readfirstlane(clamp_len(p.seq_lens[b], p.max_len));
@@ -436,8 +436,8 @@ __global__ __launch_bounds__(64 * NG) void decode_merge_kernel(DecodeParams p) {
   __shared__ float sm_M[NG];
   __shared__ float sm_den[NG];
   __shared__ float sm_num[NG][D];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int t = threadIdx.x, g = t >> 6, lane = t & 63;
+  const int h = group_x(), b = group_y();
+  const int t = thread_x(), g = t >> 6, lane = t & 63;
   const size_t pair = (size_t)b * p.H + h;
   const int nv = p.n_split;  // empty chunks carry m = -inf and weigh nothing
   const float* ml = p.ws_ml + pair * p.n_split * 2;

@@ -14,10 +14,10 @@ namespace attn {
 __global__ __launch_bounds__(64) void measure_read_kernel(const u32x4* __restrict__ p, size_t n16, size_t span,
                                                           uint32_t* sink) {
   constexpr int U = 8;
-  const size_t s0 = (size_t)blockIdx.x * span;
+  const size_t s0 = (size_t)group_x() * span;
   const size_t s1 = s0 + span < n16 ? s0 + span : n16;
   uint32_t acc = 0;
-  for (size_t i = s0 + threadIdx.x; i < s1; i += 64 * U) {
+  for (size_t i = s0 + thread_x(); i < s1; i += 64 * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -25,7 +25,7 @@ __global__ __launch_bounds__(64) void measure_read_kernel(const u32x4* __restric
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  if (acc == 0x9e3779b9u) sink[(size_t)blockIdx.x * 64 + threadIdx.x] = acc;
+  if (acc == 0x9e3779b9u) sink[(size_t)group_x() * 64 + thread_x()] = acc;
 }
 
 hipError_t launch_measure_read(const void* buf, size_t bytes, int waves, uint32_t* sink, hipStream_t st) {

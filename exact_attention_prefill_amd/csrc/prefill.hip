@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   __shared__ __attribute__((aligned(1024))) char vbuf2[XB];
   __shared__ __attribute__((aligned(1024))) char vbuf3[XB];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
   const int kgrp = __builtin_amdgcn_readfirstlane(wave / RW);  // key group (0 when KG == 1)
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(64 * NW, (prefill_waves_per_simd<D, QB>())) void pr
   // XCD-aware mapping: consecutive workgroup ids are dealt round-robin to the 8 XCDs;
   // give each XCD a contiguous run of work so the q-blocks sharing one head's K/V
   // (and hence its L2) run on the same XCD.
-  const int G = gridDim.x;
-  const int bid = blockIdx.x;
+  const int G = p.nqblk * p.H * p.B;  // the grid (one workgroup per q-block, head and batch)
+  const int bid = group_x();
   const int xcd = bid & 7, slot = bid >> 3;
   const int per = G >> 3, rem = G & 7;
   // Integer division is expanded on the VALU; pin the (uniform) results to SGPRs so
