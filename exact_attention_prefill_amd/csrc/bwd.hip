@@ -95,6 +95,42 @@ __device__ __forceinline__ u32x4 tr_read(const char* buf, int h, int s, int db, 
   return (u32x4){lo[0], lo[1], hi[0], hi[1]};
 }
 
+// The same reads from per-lane bases, for kernels short of registers.  The physical
+// chunk (2ks + half) ^ key equals 2ks ^ (half ^ key), and a row's chunk field lies in
+// bits below its row offset, so operand (h, ks) of row_read sits at
+// (row_base ^ (ks << 5)) + 32h RB: one XOR per read from one register.  Likewise the
+// transposed chunk (4db + c) ^ key equals 4db ^ (c ^ key), so tr_read's two loads sit
+// at (tr_base ^ (db << 6)) + (32h + 16s) RB, from one base per load.
+template <int D, bool DUAL>
+__device__ __forceinline__ uint32_t row_base(int lane) {
+  constexpr int RB = lds_row_bytes<D>();
+  const int row = lane & 31;
+  const int key = DUAL ? dual_key<D>(row & 15) : row_key<D>(row & 15);
+  return (uint32_t)(row * RB + (((lane >> 5) ^ key) << 4));
+}
+template <int D>
+__device__ __forceinline__ u32x4 row_read_at(const char* buf, uint32_t base, int h, int ks) {
+  constexpr int RB = lds_row_bytes<D>();
+  return lds_read_b128((const uint16_t*)buf, (base ^ (uint32_t)(ks << 5)) + 32 * h * RB);
+}
+template <int D>
+__device__ __forceinline__ uint32_t tr_base(int lane, int hi) {
+  constexpr int RB = lds_row_bytes<D>();
+  const int r = lane & 15, gg = (lane >> 4) & 1, half = lane >> 5;
+  const int rowlo = 4 * half + (r >> 2) + 8 * hi;
+  const int c = 2 * gg + ((r & 3) >> 1);
+  return (uint32_t)(rowlo * RB + ((c ^ dual_key<D>(rowlo)) << 4) + 8 * (r & 1));
+}
+template <int D>
+__device__ __forceinline__ u32x4 tr_read_at(const char* buf, uint32_t lo_base, uint32_t hi_base, int h, int s,
+                                            int db) {
+  constexpr int RB = lds_row_bytes<D>();
+  const uint32_t x = (uint32_t)(db << 6), o = (32 * h + 16 * s) * RB;
+  const u32x2 lo = lds_read_tr((const uint16_t*)buf, (lo_base ^ x) + o);
+  const u32x2 hi = lds_read_tr((const uint16_t*)buf, (hi_base ^ x) + o);
+  return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Stage one BN-row tile of a [rows][D] tensor into LDS: this wave's share of 1 KiB
 // LDS-direct loads; physical slot sl of row r receives logical chunk sl ^ key(r).
 // Padded rows (d = 32, 96) have slots past the data, which take a copy of a chunk of
@@ -232,12 +268,14 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 8 / NW) void bwd_dq_kernel(B
 
   // Keys visible to this lane's row: below N and (causal) at most the row.
   const int key_end = CAUSAL ? min(N, qrow + 1) : N;
+  const uint32_t kbase = row_base<D, true>(lane), vbase = row_base<D, false>(lane);
+  const uint32_t tlo = tr_base<D>(lane, 0), thi = tr_base<D>(lane, 1);
   auto unit = [&](int u, const char* kb, const char* vb, int h) __attribute__((always_inline)) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      st = mfma32x32x16<DT>(row_read<D, true>(kb, h, ks, lane), qf[ks], st);
-      dpt = mfma32x32x16<DT>(row_read<D, false>(vb, h, ks, lane), df[ks], dpt);
+      st = mfma32x32x16<DT>(row_read_at<D>(kb, kbase, h, ks), qf[ks], st);
+      dpt = mfma32x32x16<DT>(row_read_at<D>(vb, vbase, h, ks), df[ks], dpt);
     }
     f32x16 ds;
     // Entry i holds key 32u + 4half + 8(i/4) + i%4: visible iff its offset 8(i/4) + i%4
@@ -258,7 +296,7 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 8 / NW) void bwd_dq_kernel(B
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(tr_read<D>(kb, h, s, db, lane), dsf[s], dqa[db]);
+      for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(tr_read_at<D>(kb, tlo, thi, h, s, db), dsf[s], dqa[db]);
   };
 
   // Tile t from (kb, vb); the loop is unrolled over the two buffer pairs so that every
