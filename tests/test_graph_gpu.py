@@ -69,3 +69,51 @@ def test_graph_replays_match_eager():
         # eager work between replays, on the same buffers
         work()
         torch.cuda.synchronize()
+
+
+def test_graph_replays_no_alloc_and_split_merge():
+    """The calls meant for callers that capture: decode with its partials in the
+    library's fixed scratch array (attn_decode_noalloc), and the decode's two passes as
+    separate calls (attn_decode_split, attn_decode_merge) on a caller workspace.  Every
+    replay, with eager work between, equals the eager results bit for bit."""
+    q, kc, vc, lens = (t.to(DEV) for t in W.decode_inputs(8, 12, 4096, 64, "f16", 0))
+    qg, kg, vg, lg = (t.to(DEV) for t in W.decode_inputs_gqa(4, 32, 8, 900, 128, "bf16", 7, [900, 5, 450, 77]))
+    out_na = torch.empty_like(q)
+    out_gq = torch.empty_like(qg)
+    out_sm = torch.empty_like(q)
+    chunk = 192
+    ws = torch.empty(ea.decode_workspace_bytes(8, 12, -(-4096 // chunk), 64), dtype=torch.uint8, device=DEV)
+
+    def work():
+        ea.decode_noalloc(q, kc, vc, lens, out_na, scale=0.125)
+        ea.decode_noalloc(qg, kg, vg, lg, out_gq, scale=0.09, chunk=64)
+        ea.decode_split(q, kc, vc, lens, scale=0.125, chunk=chunk, workspace=ws)
+        ea.decode_merge(ws, out_sm, max_len=4096, chunk=chunk)
+
+    work()  # the first no-alloc call on a device also looks up the scratch address
+    torch.cuda.synchronize()
+    ref = [bits(t) for t in (out_na, out_gq, out_sm)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        for t in (out_na, out_gq, out_sm):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [bits(t) for t in (out_na, out_gq, out_sm)]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), (rep, i)
+        work()
+        torch.cuda.synchronize()
