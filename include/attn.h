@@ -22,9 +22,10 @@
  *     All tensors of one call share one element type (attn_dtype); the output has the
  *     input's type, rounded from fp32 to nearest-even.
  *   - Pointers are DEVICE pointers (except where a parameter says host) owned by the
- *     caller; they must be non-null and 16-byte aligned.  The library keeps no
- *     allocation and no state between calls other than a thread-local error text and
- *     a per-device compute-unit count.
+ *     caller; they must be non-null and 16-byte aligned (seq_lens and lse: 4-byte).
+ *     The library keeps no allocation and no state between calls other than a
+ *     thread-local error text, a per-device compute-unit count and the per-device
+ *     scratch array of attn_decode_noalloc (part of the code object, not allocated).
  *   - `stream` is a hipStream_t (NULL selects the default stream).  Calls enqueue
  *     work on it and return without waiting; kernel faults surface on later
  *     synchronisation, launch failures are reported as ATTN_ERR_HIP.
@@ -84,7 +85,8 @@ int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* 
  * k_cache, v_cache, seq_lens, scale)).
  *   q        : [B][H][1][d] one query row per sequence and head;
  *   k_cache, v_cache : [B][H][max_len][d];
- *   seq_lens : DEVICE int32 [B]; sequence b attends to cache rows 0 .. seq_lens[b]-1
+ *   seq_lens : DEVICE int32 [B], 4-byte aligned; sequence b attends to cache rows
+ *              0 .. seq_lens[b]-1
  *              (the current token's own row included, so decoding token t with
  *              seq_lens = t + 1 equals causal prefill row t).  Valid lengths are
  *              1 .. max_len; the kernels clamp other values into [0, max_len] for
