@@ -47,6 +47,15 @@ int check_common(int B, int H, int rows, int d, int dtype, float scale, const ch
   return ATTN_OK;
 }
 
+// The decode kernels carry the batch and the head (or head group) in the launch grid's
+// second and third dimensions, whose limit is 65535.
+constexpr int kDecodeGridMax = 65535;
+int check_decode_grid(int B, int H) {
+  if (B > kDecodeGridMax || H > kDecodeGridMax)
+    return fail(ATTN_ERR_INVALID_ARG, "decode takes B and H up to %d (B=%d, H=%d)", kDecodeGridMax, B, H);
+  return ATTN_OK;
+}
+
 int check_heads(int H, int Hkv) {
   if (Hkv < 1 || Hkv > H || H % Hkv != 0)
     return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must divide the query head count H=%d", Hkv, H);
@@ -261,6 +270,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
                        int passes = attn::kDecodeSplitPass | attn::kDecodeMergePass) {
   int st;
   if ((st = check_common(B, H, max_len, d, dtype, scale, "max_len")) != ATTN_OK) return st;
+  if ((st = check_decode_grid(B, H)) != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")))
     return st;
@@ -361,6 +371,7 @@ int attn_decode_merge(const void* workspace, size_t ws_bytes, void* out, int B, 
                       int chunk, void* stream) {
   int st;
   if ((st = check_common(B, Hq, max_len, d, dtype, 1.f, "max_len")) != ATTN_OK) return st;
+  if ((st = check_decode_grid(B, Hq)) != ATTN_OK) return st;
   if ((st = check_ptr(out, "out")) || (st = check_ptr(workspace, "workspace"))) return st;
   if (out == workspace) return fail(ATTN_ERR_INVALID_ARG, "out must not alias the workspace");
   const int T = ATTN_DECODE_ROW_GRANULE;

@@ -92,6 +92,8 @@ int attn_prefill_plan(int B, int H, int N, int d, int causal, int num_cus, int* 
  *              1 .. max_len; the kernels clamp other values into [0, max_len] for
  *              memory safety and write zeros for a length of 0.
  *   out      : [B][H][1][d].
+ *   B and H at most 65535 (the launch grid carries them in dimensions of that limit;
+ *   larger values return ATTN_ERR_INVALID_ARG), here and in every decode entry point.
  * The chunk size is chosen at launch (attn_decode_choose_split with this device's
  * compute-unit count).  The partials live in a workspace taken with hipMallocAsync and
  * released with hipFreeAsync on `stream` (stream ordered, no synchronisation). */

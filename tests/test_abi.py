@@ -92,6 +92,8 @@ def _decode_ex(**kw):
         (dict(ws_bytes=100), ea.ATTN_ERR_WORKSPACE),
         (dict(scale=float("-inf")), ea.ATTN_ERR_INVALID_ARG),
         (dict(out=P[1]), ea.ATTN_ERR_INVALID_ARG),
+        (dict(B=65536, max_len=32, chunk=32), ea.ATTN_ERR_INVALID_ARG),  # the launch grid's batch limit
+        (dict(B=1, H=65536, max_len=32, chunk=32), ea.ATTN_ERR_INVALID_ARG),  # and its head limit
     ],
 )
 def test_decode_validation(kw, status):
@@ -173,6 +175,7 @@ def _decode_gqa(**kw):
         (dict(Hkv=4), ea.ATTN_ERR_INVALID_ARG),
         (dict(Hkv=0), ea.ATTN_ERR_INVALID_ARG),
         (dict(Hkv=12), ea.ATTN_ERR_INVALID_ARG),
+        (dict(B=65536, max_len=32, chunk=32), ea.ATTN_ERR_INVALID_ARG),  # the launch grid's batch limit
         (dict(chunk=48), ea.ATTN_ERR_INVALID_ARG),
         (dict(lens=None), ea.ATTN_ERR_INVALID_ARG),
         (dict(ws_bytes=ea.decode_workspace_bytes(2, 6, 4, 128) - 1), ea.ATTN_ERR_WORKSPACE),
@@ -274,6 +277,7 @@ def test_noalloc_decode_validation():
     assert call(1, 6, 4, 64, 64, 0) == ea.ATTN_ERR_INVALID_ARG  # Hkv does not divide H
     assert call(1, 1, 1, 64, 80, 0) == ea.ATTN_ERR_UNSUPPORTED
     assert call(1, 1, 1, 64, 64, 48) == ea.ATTN_ERR_INVALID_ARG  # not a multiple of the granule
+    assert call(65536, 1, 1, 32, 32, 0) == ea.ATTN_ERR_INVALID_ARG  # the launch grid's batch limit
     assert ea.decode_workspace_bytes(64, 32, 128, 64) > ea.DECODE_SCRATCH_BYTES
     assert call(64, 32, 32, 4096, 64, 32) == ea.ATTN_ERR_WORKSPACE
     assert "scratch" in ea.last_error()
@@ -297,6 +301,9 @@ def test_decode_pass_and_read_validation():
     assert merge(0, need) == ea.ATTN_ERR_INVALID_ARG
     assert merge(32, need, out=P[5]) == ea.ATTN_ERR_INVALID_ARG  # out aliases the workspace
     assert merge(32, need, out=None) == ea.ATTN_ERR_INVALID_ARG
+    big = lambda B, H: L.attn_decode_merge(P[5], 1 << 40, P[3], B, H, 32, 64, 0, 32, None)  # noqa: E731
+    assert big(65536, 1) == ea.ATTN_ERR_INVALID_ARG  # the launch grid's batch limit
+    assert big(1, 65536) == ea.ATTN_ERR_INVALID_ARG
     read = lambda nbytes, waves, sink_bytes: L.attn_measure_read(P[0], nbytes, waves, P[6], sink_bytes, None)  # noqa: E731
     assert read(100, 1, 256) == ea.ATTN_ERR_INVALID_ARG  # not a multiple of 16
     assert read(1024, 0, 256) == ea.ATTN_ERR_INVALID_ARG
