@@ -46,6 +46,17 @@ MUTATIONS = {
     "split_den_unweighted": ("den = sum(w * l for w, l in zip(wts, ls))", "den = sum(ls)"),
     "split_sign": ("wts = [np.exp(m - M) for m in ms]", "wts = [np.exp(M - m) for m in ms]"),
     "split_drops_last_row": ("c1 = min(L, c0 + chunk)", "c1 = min(L - 1, c0 + chunk)"),
+    "split_acc_unweighted": ("num = sum(w * a for w, a in zip(wts, accs))", "num = sum(accs)"),
+    "split_unscaled": ("s = float(scale) * (kc[b, g, c0:c1] @ q[b, h, 0])", "s = (kc[b, g, c0:c1] @ q[b, h, 0])"),
+    "decode_unscaled": ("s = float(scale) * (q[b, h] @ kc[b, g, :L].T)", "s = (q[b, h] @ kc[b, g, :L].T)"),
+    "bwd_dq_unscaled": ("dq[b, h] = float(scale) * (ds @ k[b, g])", "dq[b, h] = (ds @ k[b, g])"),
+    "bwd_dv_scaled": ("dv[b, g] += pm.T @ do[b, h]", "dv[b, g] += float(scale) * (pm.T @ do[b, h])"),
+    "bwd_ds_sign": ("ds = pm * (dp - np.sum(dp * pm, axis=1, keepdims=True))",
+                    "ds = pm * (np.sum(dp * pm, axis=1, keepdims=True) - dp)"),
+    "bwd_rows_dq_unscaled": ("return float(scale) * (ds @ kh)", "return ds @ kh"),
+    "bwd_rows_dv_from_ds": ("dv += pm[:, keys].T @ doh[rows]", "dv += ds[:, keys].T @ doh[rows]"),
+    "bwd_rows_values_unmasked": ("s = np.where(np.arange(kh.shape[0]) <= rows[:, None], s, -np.inf)",
+                                 "s = s"),
 }
 
 
