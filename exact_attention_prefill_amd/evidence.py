@@ -290,6 +290,15 @@ def summarize(out: str):
         bank, active = median_counter(lds, "SQ_LDS_BANK_CONFLICT"), median_counter(lds, "SQ_LDS_IDX_ACTIVE")
         if bank is not None and active:
             r["lds_conflict_frac"] = bank / active
+        # Wave time: the wave-cycles spent issuing, waiting to issue (a dependence or a
+        # busy unit) and waiting on counters or barriers add up to SQ_WAVE_CYCLES.
+        wv = kernel_slices(key, pmc.get("wave", []), "pmc")
+        cyc = median_counter(wv, "SQ_WAVE_CYCLES")
+        if cyc:
+            for part, counter in (("issuing", "SQ_ACTIVE_INST_ANY"), ("waiting_issue", "SQ_WAIT_INST_ANY"),
+                                  ("waiting_counters", "SQ_WAIT_ANY")):
+                v = median_counter(wv, counter)
+                r["wave_" + part] = v / cyc if v is not None else None
         rows[key] = r
 
     pre = rec["config"]["prefill"] if rec else {"B": 1, "H": 16, "N": 16384, "d": 128, "causal": False}
@@ -359,15 +368,18 @@ def render(out, rows, derived, agent, fc, wc, sha):
               f"HBM calibration (a plain {CALIBRATE_MIB} MiB device copy in the same process): FETCH_SIZE x "
               f"{_fmt(fc, '.4f')}, WRITE_SIZE x {_fmt(wc, '.4f')}.", "",
               "| kernel | dispatches | avg us | min us | HBM MB (cal.) | MFMA busy | by MFMA count | "
-              "VALU+MFMA both busy | clock GHz | LDS conflict cycles |",
-              "|---|---|---|---|---|---|---|---|---|---|"]
+              "VALU+MFMA both busy | clock GHz | LDS conflict cycles | wave time: issuing / waiting to issue / "
+              "waiting on counters or barriers |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for key, r in rows.items():
         hbm = r.get("hbm_bytes")
         lines.append(
             f"| `{KERNELS[key]}` | {r['dispatches']} | {_fmt(r['avg_us'], '.2f')} | {_fmt(r['min_us'], '.2f')} | "
             f"{_fmt(hbm / 1e6 if hbm is not None else None, '.2f')} | {_fmt(r.get('mfma_busy'), '.1%')} | "
             f"{_fmt(r.get('mfma_busy_from_insts'), '.1%')} | {_fmt(r.get('coexec'), '.1%')} | "
-            f"{_fmt(r.get('clock_ghz'), '.2f')} | {_fmt(r.get('lds_conflict_frac'), '.1%')} |")
+            f"{_fmt(r.get('clock_ghz'), '.2f')} | {_fmt(r.get('lds_conflict_frac'), '.1%')} | "
+            f"{_fmt(r.get('wave_issuing'), '.0%')} / {_fmt(r.get('wave_waiting_issue'), '.0%')} / "
+            f"{_fmt(r.get('wave_waiting_counters'), '.0%')} |")
     d = derived
     hb, ab = d["prefill_hbm_bytes"], d["prefill_algorithmic_bytes"]
     lines += ["",

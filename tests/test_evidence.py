@@ -122,6 +122,12 @@ def run_dir(tmp_path):
           (SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * n_pmc
     mf += [(SPLIT, 1, {"GRBM_GUI_ACTIVE": 1.0}), (MERGE, 1, {"GRBM_GUI_ACTIVE": 1.0})] * (2 * ev.PMC_DECODE_ITERS)
     _pmc(os.path.join(out, "mfma", "h", "run_counter_collection.csv"), mf)
+    # Wave pass: 1e6 wave-cycles, 30% issuing, 50% waiting to issue, 20% on counters or barriers.
+    wv = [(PRE, 1_000_000, {"SQ_WAVE_CYCLES": 1.0e6, "SQ_ACTIVE_INST_ANY": 3.0e5, "SQ_WAIT_INST_ANY": 5.0e5,
+                            "SQ_WAIT_ANY": 2.0e5}),
+          (SPLIT, 1, {"SQ_WAVE_CYCLES": 1.0}), (MERGE, 1, {"SQ_WAVE_CYCLES": 1.0})] * n_pmc
+    wv += [(SPLIT, 1, {"SQ_WAVE_CYCLES": 1.0}), (MERGE, 1, {"SQ_WAVE_CYCLES": 1.0})] * (2 * ev.PMC_DECODE_ITERS)
+    _pmc(os.path.join(out, "wave", "h", "run_counter_collection.csv"), wv)
     return out
 
 
@@ -144,6 +150,9 @@ def test_summary_derivations(run_dir):
     s = json.load(open(os.path.join(run_dir, "summary.json")))
     assert s["kernels"]["prefill"]["mfma_busy_from_insts"] == pytest.approx(0.5)
     assert s["kernels"]["prefill"]["coexec"] == pytest.approx(0.1)
+    assert s["kernels"]["prefill"]["wave_issuing"] == pytest.approx(0.3)
+    assert s["kernels"]["prefill"]["wave_waiting_issue"] == pytest.approx(0.5)
+    assert s["kernels"]["prefill"]["wave_waiting_counters"] == pytest.approx(0.2)
     assert s["calibration"] == {"fetch": pytest.approx(2.0), "write": pytest.approx(1.0)}
     c = json.load(open(os.path.join(run_dir, "prefill_headline_counters.json")))
     assert c["kernel_sha"] == ev.source_hash(ev.PREFILL_SOURCES)
@@ -151,6 +160,7 @@ def test_summary_derivations(run_dir):
     assert c["algorithmic_bytes_per_launch"] == 4 * 16 * 16384 * 128 * 2
     md = open(os.path.join(run_dir, "summary.md")).read()
     assert "python3 -u bench.py" in md and PRE in md
+    assert "30% / 50% / 20%" in md
 
 
 def test_stored_traffic_key_matches_what_bench_hashes():
